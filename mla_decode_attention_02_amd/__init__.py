@@ -1,0 +1,18 @@
+"""Paged MLA decode attention for AMD Instinct MI355X (gfx950).
+
+The compute runs in the HIP library ``libmla_decode.so`` (C ABI, declared in
+``include/mla_decode.h``); this package only marshals torch tensors into that
+ABI.  Importing the package does not load the library; the first call does,
+and raises if the library has not been built.
+"""
+
+__all__ = ["get_metadata", "get_metadata_shape", "workspace_size", "mla_decode",
+           "mla_decode_splitkv", "mla_decode_combine", "library_path"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import api
+
+        return getattr(api, name)
+    raise AttributeError(name)

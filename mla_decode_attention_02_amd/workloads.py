@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for paged MLA decode.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic, so both the HIP path and the CPU oracle can consume what
+it produces.
+
+Layout (shared by every consumer):
+  q            [B, s_q, h_q, 576]        bf16/fp16
+  k_cache      [num_pages, 64, 1, 576]   bf16/fp16   (one latent KV head)
+  block_table  [B, max_pages]            int32       (-1 past a request's pages)
+  cache_seqlens[B]                       int32
+
+Recipe (fixed so that every run reproduces the same tensors):
+  g = torch.Generator('cpu').manual_seed(seed), then in this order
+    1. seqlens: fixed list, or torch.randint(lo, hi + 1, (B,), generator=g)
+    2. perm = torch.randperm(N, generator=g), N = sum_b ceil(n_b / 64) + extra
+       pages; request b takes the next ceil(n_b / 64) entries of perm
+    3. q = torch.randn(B, s_q, h_q, 576, generator=g) * sigma
+    4. k = torch.randn(N, 64, 1, 576, generator=g) * sigma
+    5. both cast to the dtype (round to nearest even)
+  Optional poison (correctness runs only): cache slots at positions >= n_b in a
+  request's last page, and every page no request uses, are overwritten with
+  +-POISON along the sign of the request's first query row, so that any read of
+  them would dominate the softmax and the output.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+D_K = 576
+D_V = 512
+PAGE = 64
+POISON = 64.0
+
+_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic decode workload (shapes, distribution, seed)."""
+
+    name: str
+    batch: int
+    s_q: int
+    h_q: int
+    dtype: str
+    sigma: float
+    causal: bool
+    seqlens: Optional[Sequence[int]] = None      # fixed lengths, or
+    seqlen_range: Optional[tuple] = None          # inclusive (lo, hi) uniform integers
+    seed: int = 0
+    description: str = field(default="", compare=False)
+
+    @property
+    def rows(self) -> int:
+        return self.s_q * self.h_q
+
+
+# The five workloads the measurements are quoted on.  Seeds are the index.
+WORKLOADS = {
+    1: Workload("tiny", 2, 1, 16, "bf16", 1.0, False, seqlens=(64, 100), seed=1,
+                description="B2 s_q1 h_q16 bf16, s_k {64,100}, non-causal"),
+    2: Workload("bs64_hq128_sk4096", 64, 1, 128, "bf16", 1.0, False, seqlens=(4096,) * 64, seed=2,
+                description="B64 s_q1 h_q128 bf16, every s_k 4096"),
+    3: Workload("varlen_bs128_hq16", 128, 1, 16, "bf16", 1.0, False, seqlen_range=(1, 8192), seed=3,
+                description="B128 s_q1 h_q16 bf16, s_k ~ U[1,8192]"),
+    4: Workload("multitoken_bs32_sq2_hq128", 32, 2, 128, "fp16", 0.5, True,
+                seqlen_range=(12288, 16384), seed=4,
+                description="B32 s_q2 h_q128 fp16 causal, s_k ~ U[12288,16384], sigma 0.5"),
+    5: Workload("longctx_bs4_hq128", 4, 1, 128, "bf16", 1.0, False,
+                seqlens=(65536, 98304, 131072, 131072), seed=5,
+                description="B4 s_q1 h_q128 bf16, s_k {64K,96K,128K,128K}"),
+}
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    block_table: torch.Tensor
+    cache_seqlens: torch.Tensor
+    softmax_scale: float
+    causal: bool
+    dtype: str
+
+    def to(self, device) -> "DecodeInputs":
+        return DecodeInputs(self.q.to(device), self.k_cache.to(device),
+                            self.block_table.to(device), self.cache_seqlens.to(device),
+                            self.softmax_scale, self.causal, self.dtype)
+
+
+def pages_of(n: int) -> int:
+    return (int(n) + PAGE - 1) // PAGE
+
+
+def make_inputs(batch: int, s_q: int, h_q: int, dtype: str = "bf16", *,
+                seqlens: Optional[Sequence[int]] = None,
+                seqlen_range: Optional[tuple] = None,
+                sigma: float = 1.0, causal: bool = False, seed: int = 0,
+                extra_pages: int = 0, poison: bool = False,
+                max_pages: Optional[int] = None) -> DecodeInputs:
+    """Draw one seeded workload following the recipe in the module docstring."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    if seqlens is not None:
+        sl = torch.tensor([int(x) for x in seqlens], dtype=torch.int64)
+        if sl.numel() != batch:
+            raise ValueError("len(seqlens) != batch")
+    elif seqlen_range is not None:
+        lo, hi = seqlen_range
+        sl = torch.randint(int(lo), int(hi) + 1, (batch,), generator=g, dtype=torch.int64)
+    else:
+        raise ValueError("give seqlens or seqlen_range")
+    n_pages = [pages_of(n) for n in sl.tolist()]
+    used = sum(n_pages)
+    total = used + int(extra_pages)
+    perm = torch.randperm(total, generator=g) if total > 0 else torch.zeros(0, dtype=torch.int64)
+    width = max(max(n_pages) if n_pages else 0, 1)
+    if max_pages is not None:
+        if max_pages < width:
+            raise ValueError("max_pages smaller than the longest request")
+        width = max_pages
+    bt = torch.full((batch, width), -1, dtype=torch.int32)
+    pos = 0
+    for b, p in enumerate(n_pages):
+        bt[b, :p] = perm[pos:pos + p].to(torch.int32)
+        pos += p
+    tdt = _DTYPES[dtype]
+    q = (torch.randn(batch, s_q, h_q, D_K, generator=g) * sigma).to(tdt)
+    k = (torch.randn(max(total, 1), PAGE, 1, D_K, generator=g) * sigma).to(tdt)
+    if poison:
+        _poison(q, k, bt, sl, perm[used:] if total > used else None)
+    return DecodeInputs(q=q, k_cache=k, block_table=bt,
+                        cache_seqlens=sl.to(torch.int32),
+                        softmax_scale=1.0 / (D_K ** 0.5), causal=causal, dtype=dtype)
+
+
+def _poison(q, k, bt, sl, unused_pages):
+    for b in range(q.shape[0]):
+        n = int(sl[b])
+        p = pages_of(n)
+        direction = torch.sign(q[b, 0, 0].float())
+        direction[direction == 0] = 1.0
+        row = (direction * POISON).to(k.dtype)
+        if p > 0 and n % PAGE != 0:
+            page = int(bt[b, p - 1])
+            k[page, n % PAGE:, 0, :] = row
+    if unused_pages is not None and unused_pages.numel() > 0:
+        k[unused_pages] = POISON
+
+
+def workload_inputs(index: int, poison: bool = False, **overrides) -> DecodeInputs:
+    """Inputs of one of the five named workloads (seed = index)."""
+    w = WORKLOADS[int(index)]
+    kw = dict(seqlens=w.seqlens, seqlen_range=w.seqlen_range, sigma=w.sigma,
+              causal=w.causal, seed=w.seed, poison=poison)
+    kw.update(overrides)
+    return make_inputs(w.batch, w.s_q, w.h_q, w.dtype, **kw)
+
+
+def workload_seqlens(index: int) -> List[int]:
+    """Only the sequence lengths of a named workload (cheap: no tensors)."""
+    w = WORKLOADS[int(index)]
+    if w.seqlens is not None:
+        return list(w.seqlens)
+    g = torch.Generator("cpu").manual_seed(int(w.seed))
+    lo, hi = w.seqlen_range
+    return torch.randint(int(lo), int(hi) + 1, (w.batch,), generator=g, dtype=torch.int64).tolist()

@@ -1,0 +1,29 @@
+"""CPU reference (oracle) for paged MLA decode attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call, link or
+execute anything in this package: only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` use it.  It
+shares no code with the HIP library (no kernels, headers, helpers, tables or
+pre/post-processing); the only thing both sides consume is the seeded input
+generator, which holds none of the method's arithmetic.
+
+Modules
+-------
+decode    exact attention over the paged latent KV cache, fp64 (NumPy), plus a
+          pure-Python brute force for tiny shapes and a merge-by-LSE of partial
+          results.
+metadata  integer re-derivation of the split-KV tile schedule.
+"""
+
+from .decode import (  # noqa: F401
+    oracle_decode,
+    oracle_decode_rows,
+    brute_force_decode,
+    oracle_partial,
+    oracle_merge,
+    visible_keys,
+    D_K,
+    D_V,
+    PAGE,
+)
+from .metadata import oracle_metadata, schedule_chunks  # noqa: F401
