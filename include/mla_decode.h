@@ -1,0 +1,198 @@
+/*
+ * mla_decode.h - C ABI of the paged MLA decode library (libmla_decode.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Multi-head latent attention at decode time: for every
+ * request b, new query token i < s_q and query head h < h_q,
+ *     s_j  = softmax_scale * <q[b,i,h,0:576], K_j>      over visible keys j
+ *     O    = sum_j softmax(s)_j * V_j,   V_j = K_j[0:512]
+ *     LSE  = log sum_j exp(s_j)          (natural log)
+ * where K_j is cached token j of request b, a 576-wide row (512 latent + 64
+ * rope columns) stored in 64-token pages reached through a block table, and one
+ * cached row serves all h_q heads.
+ *   Sources: page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析"
+ *   (blog.hotdry.top), sections "计算边界特性与优化方向抉择" (FLOPs
+ *   2*h_q*s_q*s_k*(d_k+d_v) over 2*s_k*d_k bytes: one shared latent row per
+ *   token) and "辅助优化：可编程依赖启动与瓦片调度" (a split-KV kernel, a combine
+ *   kernel, a tile scheduler); page "FlashMLA: 高性能GPU注意力机制计算库
+ *   文件结构分析" (hanhandi.cn), sections "项目主要功能" (bf16/fp16, paged KV
+ *   cache with block size 64), "6. SM资源调度优化" (scheduler quota) and
+ *   "火辣点评：FlashMLA的类设计" (only d_k = 576 / d_v = 512; errors printed
+ *   followed by exit(1), which this library replaces with status codes);
+ *   page "FlashAttention终极指南：如何通过动态计算图实现3倍推理加速"
+ *   (cnnetsun.cn), sections "核心代码实现解析" (cache_seqlens, causal) and
+ *   "问题二：精度偏差处理" (softmax LSE returned next to the output).
+ *
+ * Readings where the pages are silent: causal masking with s_q > 1 is
+ * bottom-right aligned (token i sees keys j <= n - s_q + i); a row that sees no
+ * key gets O = 0 and LSE = -inf; cache slots past a request's length and
+ * block-table entries past its last page are never read.
+ *
+ * Conventions for every entry point.
+ *  - Pointers marked "device" are HIP device pointers; the caller owns every
+ *    buffer; the library allocates no device memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Entry points only
+ *    enqueue work on it and never synchronise; a successful return means the
+ *    work was enqueued.
+ *  - Host-side argument checks happen before anything is enqueued: on failure
+ *    nothing is enqueued, a status is returned and mla_last_error() describes
+ *    it.  The process is never terminated.
+ *  - Preconditions NOT checked on the host (violating them is undefined
+ *    behaviour): 0 <= cache_seqlens[b] <= max_pages_per_seq * 64; the entries
+ *    block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages);
+ *    `sched` / `split_offsets` were produced by mla_get_metadata from the same
+ *    cache_seqlens with the same num_parts; cache contents are finite.
+ *  - Thread safety: all entry points may be called concurrently; the error
+ *    text is kept per thread.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+#define MLA_D_K 576             /* cached row width = query width           */
+#define MLA_D_V 512             /* value width: the first 512 columns       */
+#define MLA_PAGE_SIZE 64        /* tokens per KV-cache page                 */
+#define MLA_SCHED_FIELDS 8      /* int32 per scheduler partition            */
+#define MLA_FIXED_OVERHEAD 5    /* per-piece overhead, in pages (scheduler) */
+
+typedef enum {
+  MLA_SUCCESS = 0,
+  MLA_ERROR_INVALID_VALUE = 1,      /* bad pointer, size, stride or alignment  */
+  MLA_ERROR_UNSUPPORTED = 2,        /* d_k != 576, d_v != 512, page != 64,      */
+                                    /* h_kv != 1, unknown dtype                 */
+  MLA_ERROR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERROR_HIP = 4                 /* a HIP runtime call or launch failed      */
+} mla_status;
+
+typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
+
+/* Text of the last error raised on the calling thread ("" if none); never NULL.
+ * The pointer stays valid until the next call into the library on this thread. */
+const char* mla_last_error(void);
+
+/* MLA_ABI_VERSION of the loaded library. */
+int mla_abi_version(void);
+
+/*
+ * Tile-scheduler shape.  The scheduler (page "FlashMLA: 高性能GPU注意力机制计算库
+ * 文件结构分析", section "6. SM资源调度优化") splits the work of all requests,
+ * counted in 64-token pages, over `num_parts` partitions.  Each partition is
+ * processed by ceil(s_q*h_q / M) workgroups, one per M-row query tile, where
+ * M = 16 when s_q*h_q <= 16 and 64 otherwise.  num_parts is chosen so that
+ * num_parts * ceil(s_q*h_q / M) fills the device once.
+ *   num_cus              compute units to fill; 0 = query the current device.
+ *   batch, s_q, h_q      > 0.   h_kv must be 1.
+ *   num_parts (out)      suggested partition count (>= 1).
+ *   sched_elems (out)    int32 elements of the `sched` array: num_parts * 8.
+ *   split_offsets_elems (out) int32 elements of `split_offsets`: batch + 1.
+ * Errors: INVALID_VALUE (sizes <= 0, null out-pointers), UNSUPPORTED (h_kv != 1),
+ * HIP (device query failed).
+ */
+mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int h_kv,
+                                  int* num_parts, int* sched_elems, int* split_offsets_elems);
+
+/*
+ * Build the split-KV tile schedule on the device (one small kernel).
+ * Every nonempty request b costs P_b + F, P_b = ceil(cache_seqlens[b] / 64),
+ * F = MLA_FIXED_OVERHEAD; quota Q = ceil(sum of costs / num_parts) + F
+ * (the page's formula).  Partitions are filled greedily in request order: a
+ * request (or its remainder) that fits the remaining budget is taken whole,
+ * otherwise the partition takes (budget - F) of its pages when that is positive
+ * and closes.
+ *   cache_seqlens  device int32 [batch], each >= 0.
+ *   num_parts      >= 1 (normally from mla_get_metadata_shape).
+ *   sched          device int32 [num_parts][8], written.  Row p =
+ *                  (begin_req, begin_page, end_req, end_page, begin_split,
+ *                   n_chunks, 0, 0): partition p covers request begin_req from
+ *                  page begin_page, all requests strictly between, and request
+ *                  end_req up to page end_page (exclusive); begin_split is the
+ *                  index of its first piece among the pieces of begin_req.
+ *                  Empty partition: (0, 0, -1, 0, 0, 0, 0, 0).
+ *   split_offsets  device int32 [batch + 1], written: exclusive prefix sum of
+ *                  the number of pieces of each request (0 for empty requests).
+ * The result depends only on (cache_seqlens, num_parts) and is reused by every
+ * layer of a decode step.  Errors: INVALID_VALUE, UNSUPPORTED, HIP.
+ */
+mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                            int num_parts, int32_t* sched, int32_t* split_offsets, void* stream);
+
+/*
+ * Bytes of device workspace mla_decode needs: fp32 partial outputs and LSEs for
+ * up to (batch + num_parts) request pieces of s_q*h_q rows each
+ * ((batch + num_parts) * s_q * h_q * (512 + 1) * 4 bytes, rounded up to 256).
+ * Errors: INVALID_VALUE.
+ */
+mla_status mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes);
+
+/* Arguments of mla_decode.  Strides are in ELEMENTS; the innermost (feature)
+ * dimension of q, k_cache and out must be contiguous (stride 1). */
+typedef struct {
+  int dtype;                   /* mla_dtype of q, k_cache and out            */
+  int batch, s_q, h_q, h_kv;   /* h_kv must be 1                              */
+  int d_k, d_v, page_size;     /* must be 576, 512, 64                        */
+  int num_pages;               /* pages in k_cache                            */
+  int max_pages_per_seq;       /* columns of block_table                      */
+  const void* q;               /* device [batch, s_q, h_q, 576]               */
+  int64_t q_stride[3];         /*   strides of batch, token, head             */
+  const void* k_cache;         /* device [num_pages, 64, h_kv, 576]           */
+  int64_t k_stride[3];         /*   strides of page, slot, kv-head            */
+  const int32_t* block_table;  /* device [batch, max_pages_per_seq]           */
+  int64_t bt_stride;           /*   stride between rows                       */
+  const int32_t* cache_seqlens;/* device [batch]                              */
+  const int32_t* sched;        /* device, from mla_get_metadata               */
+  const int32_t* split_offsets;/* device, from mla_get_metadata               */
+  int num_parts;               /* the num_parts the schedule was built with   */
+  float softmax_scale;         /* finite, > 0 (typically 1/sqrt(576))         */
+  int causal;                  /* 0/1; bottom-right aligned when s_q > 1      */
+  void* workspace;             /* device, >= mla_workspace_size bytes, 256-B aligned */
+  size_t workspace_bytes;
+  void* out;                   /* device [batch, s_q, h_q, 512], dtype        */
+  int64_t out_stride[3];       /*   strides of batch, token, head             */
+  float* lse;                  /* device [batch, s_q, h_q] fp32, contiguous   */
+} mla_decode_args;
+
+/*
+ * Paged MLA decode: mla_decode_splitkv followed by mla_decode_combine on
+ * `stream`.  Writes out and lse for every (b, i, h).
+ * Alignment: q, k_cache, out must be 16-byte aligned, as must every stride
+ * times the element size (q_stride[*], k_stride[0..1], out_stride[*] multiples
+ * of 8); lse and the int32 arrays 4-byte aligned.
+ * Errors: INVALID_VALUE (null pointer, non-positive size, bad stride or
+ * alignment, non-finite or non-positive scale), UNSUPPORTED (dims, page size,
+ * h_kv, dtype), WORKSPACE_TOO_SMALL, HIP (launch failed).
+ */
+mla_status mla_decode(const mla_decode_args* args, void* stream);
+
+/*
+ * First phase only: the split-KV attention kernel.  Requests handled by a single
+ * partition get their final out/lse written here; the pieces of split requests
+ * go to the workspace as fp32 partial outputs with their LSE.
+ * (Page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析", section
+ * "辅助优化：可编程依赖启动与瓦片调度": the splitkv_mla kernel.)
+ * Same arguments and errors as mla_decode.
+ */
+mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream);
+
+/*
+ * Second phase only: merge the pieces of every split request by their LSE
+ *   LSE = log sum_k exp(LSE_k),  O = sum_k exp(LSE_k - LSE) * O_k
+ * and write out/lse; also writes O = 0, LSE = -inf for requests with no cached
+ * token.  Must follow mla_decode_splitkv with the same arguments on the same
+ * stream.  (Same page and section: the combine kernel.)
+ * Same arguments and errors as mla_decode.
+ */
+mla_status mla_decode_combine(const mla_decode_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

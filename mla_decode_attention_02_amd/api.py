@@ -1,0 +1,226 @@
+"""Thin torch binding of the C ABI in include/mla_decode.h.
+
+Argument marshalling only: every step of the decode path (scheduling, attention,
+combine) runs in the HIP kernels of libmla_decode.so.  torch provides device
+memory and the current stream.  There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+D_K = 576
+D_V = 512
+PAGE = 64
+SCHED_FIELDS = 8
+
+_LIB_NAME = "libmla_decode.so"
+_lib = None
+_lock = threading.Lock()
+
+DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1}
+
+
+class MlaError(RuntimeError):
+    """A status other than MLA_SUCCESS returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"mla status {status}: {message}")
+        self.status = status
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of mla_decode_args."""
+
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("batch", ctypes.c_int), ("s_q", ctypes.c_int), ("h_q", ctypes.c_int), ("h_kv", ctypes.c_int),
+        ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("page_size", ctypes.c_int),
+        ("num_pages", ctypes.c_int),
+        ("max_pages_per_seq", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("q_stride", ctypes.c_int64 * 3),
+        ("k_cache", ctypes.c_void_p), ("k_stride", ctypes.c_int64 * 3),
+        ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int64),
+        ("cache_seqlens", ctypes.c_void_p),
+        ("sched", ctypes.c_void_p), ("split_offsets", ctypes.c_void_p),
+        ("num_parts", ctypes.c_int),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", ctypes.c_int),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64 * 3),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla_decode.so (built in-tree by build.py); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m mla_decode_attention_02_amd.build`")
+        L = ctypes.CDLL(path)
+        i, p, st = ctypes.c_int, ctypes.c_void_p, ctypes.c_int
+        L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_last_error.argtypes = []
+        L.mla_abi_version.restype = ctypes.c_int
+        L.mla_abi_version.argtypes = []
+        L.mla_get_metadata_shape.restype = st
+        L.mla_get_metadata_shape.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.mla_get_metadata.restype = st
+        L.mla_get_metadata.argtypes = [p, i, i, i, i, i, p, p, p]
+        L.mla_workspace_size.restype = st
+        L.mla_workspace_size.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+        for name in ("mla_decode", "mla_decode_splitkv", "mla_decode_combine"):
+            fn = getattr(L, name)
+            fn.restype = st
+            fn.argtypes = [ctypes.POINTER(DecodeArgs), p]
+        _lib = L
+        return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MlaError(status, lib().mla_last_error().decode())
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def get_metadata_shape(batch: int, s_q: int, h_q: int, h_kv: int = 1, num_cus: int = 0) -> Tuple[int, int, int]:
+    """(num_parts, sched_elems, split_offsets_elems) for this decode shape."""
+    n, se, so = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().mla_get_metadata_shape(num_cus, batch, s_q, h_q, h_kv,
+                                        ctypes.byref(n), ctypes.byref(se), ctypes.byref(so)))
+    return n.value, se.value, so.value
+
+
+def get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int = 1,
+                 num_parts: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV tile schedule for one decode step: (sched [num_parts, 8],
+    split_offsets [batch + 1]), both int32 on the device of cache_seqlens."""
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.dim() != 1:
+        raise ValueError("cache_seqlens must be a 1-D int32 device tensor")
+    seq = cache_seqlens.contiguous()
+    batch = seq.numel()
+    if num_parts is None:
+        with torch.cuda.device(seq.device):
+            num_parts, _, _ = get_metadata_shape(batch, s_q, h_q, h_kv)
+    sched = torch.empty((num_parts, SCHED_FIELDS), dtype=torch.int32, device=seq.device)
+    offs = torch.empty((batch + 1,), dtype=torch.int32, device=seq.device)
+    _check(lib().mla_get_metadata(seq.data_ptr(), batch, s_q, h_q, h_kv, num_parts,
+                                  sched.data_ptr(), offs.data_ptr(), _stream_ptr(seq.device)))
+    return sched, offs
+
+
+def workspace_size(batch: int, s_q: int, h_q: int, num_parts: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mla_workspace_size(batch, s_q, h_q, num_parts, ctypes.byref(n)))
+    return n.value
+
+
+def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
+                workspace, out, lse) -> DecodeArgs:
+    a = DecodeArgs()
+    a.dtype = DTYPE_CODES[q.dtype]
+    a.batch, a.s_q, a.h_q = q.shape[0], q.shape[1], q.shape[2]
+    a.h_kv = k_cache.shape[2]
+    a.d_k, a.d_v, a.page_size = q.shape[3], out.shape[3], k_cache.shape[1]
+    a.num_pages = k_cache.shape[0]
+    a.max_pages_per_seq = block_table.shape[1]
+    a.q = q.data_ptr()
+    a.q_stride[:] = list(q.stride()[:3])
+    a.k_cache = k_cache.data_ptr()
+    a.k_stride[:] = list(k_cache.stride()[:3])
+    a.block_table = block_table.data_ptr()
+    a.bt_stride = block_table.stride(0)
+    a.cache_seqlens = cache_seqlens.data_ptr()
+    a.sched = sched.data_ptr()
+    a.split_offsets = offs.data_ptr()
+    a.num_parts = sched.shape[0]
+    a.softmax_scale = float(softmax_scale)
+    a.causal = 1 if causal else 0
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.out = out.data_ptr()
+    a.out_stride[:] = list(out.stride()[:3])
+    a.lse = lse.data_ptr()
+    return a
+
+
+def _validate_tensors(q, k_cache, block_table, cache_seqlens):
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError("q must be bf16 or fp16")
+    if k_cache.dtype != q.dtype:
+        raise ValueError("k_cache dtype must match q")
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2 or cache_seqlens.dim() != 1:
+        raise ValueError("expected q [B,s_q,h_q,576], k_cache [pages,64,1,576], block_table [B,P], cache_seqlens [B]")
+    if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
+        raise ValueError("block_table and cache_seqlens must be int32")
+    for t in (q, k_cache, block_table, cache_seqlens):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    if q.stride(3) != 1 or k_cache.stride(3) != 1 or block_table.stride(1) != 1:
+        raise ValueError("innermost dimensions must be contiguous")
+
+
+class DecodeBuffers:
+    """Outputs and workspace of one decode shape, allocated once and reused."""
+
+    def __init__(self, q: torch.Tensor, num_parts: int):
+        B, s_q, h_q, _ = q.shape
+        self.out = torch.empty((B, s_q, h_q, D_V), dtype=q.dtype, device=q.device)
+        self.lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+        nbytes = workspace_size(B, s_q, h_q, num_parts)
+        self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+
+
+def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+    _validate_tensors(q, k_cache, block_table, cache_seqlens)
+    if metadata is None:
+        metadata = get_metadata(cache_seqlens, q.shape[1], q.shape[2], k_cache.shape[2])
+    sched, offs = metadata
+    if buffers is None:
+        buffers = DecodeBuffers(q, sched.shape[0])
+    a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
+                    buffers.workspace, buffers.out, buffers.lse)
+    _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
+    return buffers.out, buffers.lse
+
+
+def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+               cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
+               metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+               buffers: Optional[DecodeBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged MLA decode.  Returns (out [B, s_q, h_q, 512] in q's dtype,
+    lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result
+    (computed here when omitted); `buffers` lets a caller reuse outputs."""
+    return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers)
+
+
+def mla_decode_splitkv(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+    """First phase only (the split-KV kernel)."""
+    return _call("mla_decode_splitkv", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
+                 metadata, buffers)
+
+
+def mla_decode_combine(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+    """Second phase only (merge of split pieces)."""
+    return _call("mla_decode_combine", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
+                 metadata, buffers)

@@ -1,0 +1,218 @@
+// C ABI of the paged MLA decode library: argument checks, launch geometry and
+// dispatch.  All computation happens in the kernels of mla_splitkv.hip,
+// mla_combine.hip and mla_metadata.hip; this file never touches tensor data.
+//
+// Errors are reported as status codes with a per-thread message instead of the
+// print-and-exit(1) handling criticised on page "FlashMLA: 高性能GPU注意力机制计算库
+// 文件结构分析", section "火辣点评：FlashMLA的类设计".
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mla_decode.h"
+#include "mla_common.hpp"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+mla_status ok() {
+  g_error.clear();
+  return MLA_SUCCESS;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Query-row tile: 16 rows when everything fits one MFMA tile, else 64.
+int tile_rows(int rows) { return rows <= 16 ? 16 : 64; }
+
+mla_status check_shape(int batch, int s_q, int h_q, int h_kv) {
+  if (batch <= 0 || s_q <= 0 || h_q <= 0)
+    return fail(MLA_ERROR_INVALID_VALUE, "batch, s_q and h_q must be positive (got %d, %d, %d)", batch, s_q, h_q);
+  if (h_kv != 1) return fail(MLA_ERROR_UNSUPPORTED, "only one latent KV head is supported (h_kv=%d)", h_kv);
+  const long long rows = (long long)s_q * h_q;
+  if (rows > 64LL * 65535) return fail(MLA_ERROR_INVALID_VALUE, "s_q*h_q=%lld exceeds %d", rows, 64 * 65535);
+  if ((long long)batch > 2147483647LL / 8) return fail(MLA_ERROR_INVALID_VALUE, "batch too large");
+  return MLA_SUCCESS;
+}
+
+size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
+  const size_t slots = (size_t)batch + (size_t)num_parts;
+  const size_t rows = (size_t)s_q * h_q;
+  const size_t bytes = slots * rows * (mla::kDV + 1) * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+mla_status check_decode(const mla_decode_args* a) {
+  if (!a) return fail(MLA_ERROR_INVALID_VALUE, "args is NULL");
+  if (a->dtype != MLA_DTYPE_BF16 && a->dtype != MLA_DTYPE_FP16)
+    return fail(MLA_ERROR_UNSUPPORTED, "dtype %d is not bf16 (0) or fp16 (1)", a->dtype);
+  if (a->d_k != MLA_D_K || a->d_v != MLA_D_V)
+    return fail(MLA_ERROR_UNSUPPORTED, "only d_k=576, d_v=512 are supported (got %d, %d)", a->d_k, a->d_v);
+  if (a->page_size != MLA_PAGE_SIZE)
+    return fail(MLA_ERROR_UNSUPPORTED, "page_size must be 64 (got %d)", a->page_size);
+  mla_status st = check_shape(a->batch, a->s_q, a->h_q, a->h_kv);
+  if (st != MLA_SUCCESS) return st;
+  if (a->num_pages <= 0 || a->max_pages_per_seq <= 0 || a->num_parts <= 0)
+    return fail(MLA_ERROR_INVALID_VALUE, "num_pages, max_pages_per_seq and num_parts must be positive");
+  if (!a->q || !a->k_cache || !a->block_table || !a->cache_seqlens || !a->sched || !a->split_offsets ||
+      !a->workspace || !a->out || !a->lse)
+    return fail(MLA_ERROR_INVALID_VALUE, "a required pointer is NULL");
+  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->out, 16) || !aligned(a->workspace, 16))
+    return fail(MLA_ERROR_INVALID_VALUE, "q, k_cache, out and workspace must be 16-byte aligned");
+  if (!aligned(a->lse, 4) || !aligned(a->block_table, 4) || !aligned(a->cache_seqlens, 4) ||
+      !aligned(a->sched, 4) || !aligned(a->split_offsets, 4))
+    return fail(MLA_ERROR_INVALID_VALUE, "lse and the int32 arrays must be 4-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (a->q_stride[i] <= 0 || a->q_stride[i] % 8)
+      return fail(MLA_ERROR_INVALID_VALUE, "q_stride[%d]=%lld must be a positive multiple of 8", i, (long long)a->q_stride[i]);
+    if (a->out_stride[i] <= 0 || a->out_stride[i] % 8)
+      return fail(MLA_ERROR_INVALID_VALUE, "out_stride[%d]=%lld must be a positive multiple of 8", i, (long long)a->out_stride[i]);
+  }
+  for (int i = 0; i < 2; ++i)
+    if (a->k_stride[i] <= 0 || a->k_stride[i] % 8)
+      return fail(MLA_ERROR_INVALID_VALUE, "k_stride[%d]=%lld must be a positive multiple of 8", i, (long long)a->k_stride[i]);
+  if (a->k_stride[1] < MLA_D_K)
+    return fail(MLA_ERROR_INVALID_VALUE, "k_stride[1]=%lld is smaller than a row (576)", (long long)a->k_stride[1]);
+  if ((long long)a->k_stride[1] * 2 * (MLA_PAGE_SIZE - 1) + MLA_D_K * 2 > 2147483647LL)
+    return fail(MLA_ERROR_INVALID_VALUE, "k_stride[1] too large");
+  if (a->q_stride[2] < MLA_D_K || a->out_stride[2] < MLA_D_V)
+    return fail(MLA_ERROR_INVALID_VALUE, "head strides must cover a row (q >= 576, out >= 512)");
+  if (a->bt_stride < a->max_pages_per_seq)
+    return fail(MLA_ERROR_INVALID_VALUE, "bt_stride (%lld) < max_pages_per_seq (%d)", (long long)a->bt_stride, a->max_pages_per_seq);
+  if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
+    return fail(MLA_ERROR_INVALID_VALUE, "softmax_scale must be finite and positive");
+  if (a->causal != 0 && a->causal != 1) return fail(MLA_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  const size_t need = workspace_bytes(a->batch, a->s_q, a->h_q, a->num_parts);
+  if (a->workspace_bytes < need)
+    return fail(MLA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the %zu required",
+                a->workspace_bytes, need);
+  return MLA_SUCCESS;
+}
+
+mla::DecodeParams make_params(const mla_decode_args* a) {
+  mla::DecodeParams p;
+  p.q = a->q;
+  p.q_s0 = a->q_stride[0]; p.q_s1 = a->q_stride[1]; p.q_s2 = a->q_stride[2];
+  p.k = a->k_cache;
+  p.k_s0 = a->k_stride[0]; p.k_s1 = a->k_stride[1];
+  p.block_table = a->block_table;
+  p.bt_s = a->bt_stride;
+  p.seqlens = a->cache_seqlens;
+  p.sched = a->sched;
+  p.split_offsets = a->split_offsets;
+  p.batch = a->batch; p.s_q = a->s_q; p.h_q = a->h_q;
+  p.rows = a->s_q * a->h_q;
+  p.num_parts = a->num_parts;
+  p.causal = a->causal;
+  p.scale_log2 = a->softmax_scale * mla::kLog2e;
+  p.out = a->out;
+  p.o_s0 = a->out_stride[0]; p.o_s1 = a->out_stride[1]; p.o_s2 = a->out_stride[2];
+  p.lse = a->lse;
+  const size_t slots = (size_t)a->batch + (size_t)a->num_parts;
+  p.part_o = static_cast<float*>(a->workspace);
+  p.part_lse = p.part_o + slots * (size_t)p.rows * mla::kDV;
+  return p;
+}
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_error.c_str(); }
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int h_kv, int* num_parts,
+                                  int* sched_elems, int* split_offsets_elems) {
+  mla_status st = check_shape(batch, s_q, h_q, h_kv);
+  if (st != MLA_SUCCESS) return st;
+  if (!num_parts || !sched_elems || !split_offsets_elems)
+    return fail(MLA_ERROR_INVALID_VALUE, "output pointers must not be NULL");
+  if (num_cus < 0) return fail(MLA_ERROR_INVALID_VALUE, "num_cus must be >= 0");
+  if (num_cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    if (num_cus <= 0) return fail(MLA_ERROR_HIP, "device reports %d compute units", num_cus);
+  }
+  const int rows = s_q * h_q;
+  const int m_blocks = (rows + tile_rows(rows) - 1) / tile_rows(rows);
+  int parts = num_cus / m_blocks;
+  if (parts < 1) parts = 1;
+  *num_parts = parts;
+  *sched_elems = parts * MLA_SCHED_FIELDS;
+  *split_offsets_elems = batch + 1;
+  return ok();
+}
+
+mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                            int num_parts, int32_t* sched, int32_t* split_offsets, void* stream) {
+  mla_status st = check_shape(batch, s_q, h_q, h_kv);
+  if (st != MLA_SUCCESS) return st;
+  if (num_parts <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_parts must be positive");
+  if (!cache_seqlens || !sched || !split_offsets) return fail(MLA_ERROR_INVALID_VALUE, "NULL pointer");
+  if (!aligned(cache_seqlens, 4) || !aligned(sched, 4) || !aligned(split_offsets, 4))
+    return fail(MLA_ERROR_INVALID_VALUE, "int32 arrays must be 4-byte aligned");
+  hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_parts, MLA_FIXED_OVERHEAD, sched,
+                                      split_offsets, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "metadata launch");
+  return ok();
+}
+
+mla_status mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes) {
+  if (!bytes) return fail(MLA_ERROR_INVALID_VALUE, "bytes is NULL");
+  mla_status st = check_shape(batch, s_q, h_q, 1);
+  if (st != MLA_SUCCESS) return st;
+  if (num_parts <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_parts must be positive");
+  *bytes = workspace_bytes(batch, s_q, h_q, num_parts);
+  return ok();
+}
+
+mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream) {
+  mla_status st = check_decode(args);
+  if (st != MLA_SUCCESS) return st;
+  const mla::DecodeParams p = make_params(args);
+  const int tile = tile_rows(p.rows);
+  const int m_blocks = (p.rows + tile - 1) / tile;
+  hipError_t e = mla::launch_splitkv(p, args->dtype, m_blocks, tile == 16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "split-KV launch");
+  return ok();
+}
+
+mla_status mla_decode_combine(const mla_decode_args* args, void* stream) {
+  mla_status st = check_decode(args);
+  if (st != MLA_SUCCESS) return st;
+  const mla::DecodeParams p = make_params(args);
+  hipError_t e = mla::launch_combine(p, args->dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+mla_status mla_decode(const mla_decode_args* args, void* stream) {
+  mla_status st = mla_decode_splitkv(args, stream);
+  if (st != MLA_SUCCESS) return st;
+  return mla_decode_combine(args, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+// Shared device-side definitions of the MLA decode kernels (gfx950 only).
+//
+// Notation: a cached row is 576 bf16/fp16 values (512 latent + 64 rope); V is
+// its first 512 columns; a page holds 64 consecutive tokens of one request
+// (page "FlashMLA: 高性能GPU注意力机制计算库 文件结构分析", section "项目主要功能").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mla {
+
+constexpr int kDK = 576;
+constexpr int kDV = 512;
+constexpr int kPage = 64;
+constexpr int kRowChunks = kDK * 2 / 16;          // 72 sixteen-byte chunks per row
+constexpr int kPageBytes = kPage * kDK * 2;       // 73728 bytes per page
+constexpr int kPageSlots = kPage * kRowChunks;    // 4608 chunks per page
+constexpr int kThreads = 256;                     // 4 waves of 64
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima are only raised when a row's maximum grows by more than this
+// (in log2 units); until then probabilities are at most 2^kRescaleSlack.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+// Kernel parameters (element strides; innermost dimension contiguous).
+struct DecodeParams {
+  const void* q;
+  int64_t q_s0, q_s1, q_s2;
+  const void* k;
+  int64_t k_s0, k_s1;
+  const int32_t* block_table;
+  int64_t bt_s;
+  const int32_t* seqlens;
+  const int32_t* sched;
+  const int32_t* split_offsets;
+  int batch, s_q, h_q, rows, num_parts, causal;
+  float scale_log2;         // softmax_scale * log2(e)
+  void* out;
+  int64_t o_s0, o_s1, o_s2;
+  float* lse;               // [batch * rows]
+  float* part_o;            // [slots, rows, 512] fp32
+  float* part_lse;          // [slots, rows]
+};
+
+// ---------------------------------------------------------------- dtypes --
+template <typename T> struct Dt;
+
+template <> struct Dt<__bf16> {
+  __device__ static inline f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+  // two floats -> packed pair, round to nearest even
+  __device__ static inline uint32_t pack2(float x, float y) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <> struct Dt<_Float16> {
+  __device__ static inline f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// --------------------------------------------------------------- helpers --
+// LDS image of one page (73728 bytes):
+//   value region  [64 rows][64 chunks of 16 B]  bytes      0 .. 65535  (columns 0..511)
+//   rope region   [64 rows][ 8 chunks of 16 B]  bytes  65536 .. 73727  (columns 512..575)
+// Chunks are XOR-swizzled within a row.  In the value region the key is a 4-bit
+// function of the row, so that 16 consecutive rows at one chunk (score reads)
+// and 4 consecutive rows x 2 chunks (transposed value reads) each hit distinct
+// bank groups; the rope region uses a 3-bit key for its 128-byte rows.
+constexpr int kRopeOff = 64 * 1024;
+
+__device__ __forceinline__ int swz_v(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int swz_r(int row) { return (row >> 1) & 7; }
+
+// Byte offset of the 16-byte chunk holding columns 8c..8c+7 (c < 64) of `row`.
+__device__ __forceinline__ int voff(int row, int c) { return row * 1024 + ((c ^ swz_v(row)) << 4); }
+// Byte offset of rope chunk c (c < 8, columns 512 + 8c ..) of `row`.
+__device__ __forceinline__ int roff(int row, int c) { return kRopeOff + row * 128 + ((c ^ swz_r(row)) << 4); }
+
+// Score-operand chunk ks*4 + g of `row` (ks compile-time, 0 <= g < 4): the
+// constant part of the swizzled offset is split off so that it folds into the
+// instruction's immediate offset.
+template <int KS>
+__device__ __forceinline__ int kchunk_off(int row, int g) {
+  if constexpr (KS < 16) {
+    return row * 1024 + (KS >> 2) * 256 + ((((KS & 3) * 4 + g) ^ swz_v(row)) << 4);
+  } else {
+    return kRopeOff + row * 128 + ((((KS - 16) * 4 + g) ^ swz_r(row)) << 4);
+  }
+}
+
+// Workgroup barrier that orders LDS reads and writes only: unlike
+// __syncthreads() it does not wait for outstanding global loads (the next page
+// in flight in registers).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wave index as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Uniform loads through the constant address space become scalar loads.
+template <typename T>
+__device__ __forceinline__ T ldu(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+// Maximum across lanes l, l^16, l^32, l^48 (one value per 16-lane row group).
+__device__ __forceinline__ float max_across_groups(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  u = __float_as_uint(x);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+
+__device__ __forceinline__ float sum_across_groups(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  u = __float_as_uint(x);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// One page in flight, staged in registers: 18 x 16 bytes per lane.
+struct PageStage {
+  u32x4 v[18];
+};
+
+// Issue the loads of one 64x576 page (HBM -> registers).  Wave w fetches value
+// rows 16w..16w+15 (one 1 KiB row per instruction, fully coalesced) and rope
+// rows 16w..16w+15 (8 rows per instruction).  Lane l fetches the source chunk
+// that belongs in LDS slot l of its row, i.e. chunk l ^ swizzle(row).
+__device__ __forceinline__ void stage_load(PageStage& st, const char* __restrict__ page, int64_t row_bytes,
+                                           int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = wave * 16 + j;
+    const int key = ((j & 7) << 1) | ((j >> 3) & 1);       // == swz_v(r)
+    st.v[j] = *(const u32x4*)(page + r * row_bytes + ((lane ^ key) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 8 + (lane >> 3);
+    st.v[16 + i] = *(const u32x4*)(page + r * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4));
+  }
+}
+
+// Write a staged page into an LDS page buffer (contiguous 1 KiB per instruction).
+__device__ __forceinline__ void stage_store(const PageStage& st, MLA_LDS char* buf, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) *(MLA_LDS u32x4*)(buf + (wave * 16 + j) * 1024 + lane * 16) = st.v[j];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    *(MLA_LDS u32x4*)(buf + kRopeOff + (wave * 2 + i) * 1024 + lane * 16) = st.v[16 + i];
+}
+
+// Compile-time unrolled loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Keys visible to query token `tok` of a request with n cached tokens.
+__device__ __forceinline__ int visible_count(int n, int s_q, int tok, int causal) {
+  if (!causal) return n;
+  int c = n - s_q + tok + 1;
+  return c < 0 ? 0 : (c > n ? n : c);
+}
+
+__device__ __forceinline__ u32x4 ld_lds16(const MLA_LDS char* p) {
+  return *(const MLA_LDS u32x4*)p;
+}
+
+// Transposed LDS read: within each 16-lane group, lane i receives column i of
+// the 4 x 16 block of 16-bit values whose row r, columns 4c..4c+3 are addressed
+// by lane 4r + c.
+__device__ __forceinline__ u32x2 ld_lds_tr(const MLA_LDS char* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace mla

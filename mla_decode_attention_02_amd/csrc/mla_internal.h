@@ -1,0 +1,19 @@
+// Launchers shared between the C ABI (mla_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams;
+
+// Split-KV attention: grid (num_parts, m_blocks), 256 threads.  dtype 0 = bf16, 1 = fp16.
+hipError_t launch_splitkv(const DecodeParams& p, int dtype, int m_blocks, bool narrow, hipStream_t st);
+// Merge of split pieces: grid (batch, ceil(rows / 4)), 256 threads.
+hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st);
+// Tile schedule: one workgroup.
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead,
+                           int32_t* sched, int32_t* split_offsets, hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (bf16/fp16 inputs, fp32 accumulation): max |dO| <= 1.5e-2 and
+max |dLSE| <= 1e-3 against the oracle on the same seeded inputs; the schedule
+is integer work and must be bit-exact.  Every case prints its name first so a
+failing run identifies itself.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle_decode, oracle_decode_rows, oracle_metadata
+from mla_decode_attention_02_amd import api
+from mla_decode_attention_02_amd.workloads import WORKLOADS, make_inputs, workload_inputs, workload_seqlens
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1.5e-2
+TOL_LSE = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(x, num_parts=None):
+    dev = torch.device("cuda:0")
+    g = x.to(dev)
+    meta = api.get_metadata(g.cache_seqlens, g.q.shape[1], g.q.shape[2], num_parts=num_parts)
+    out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale,
+                              g.causal, metadata=meta)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), [m.cpu().numpy() for m in meta]
+
+
+def compare(out, lse, ref_o, ref_l, tag):
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(lse)), f"{tag}: -inf pattern differs"
+    assert not np.isnan(out).any(), f"{tag}: NaN in output"
+    do = np.abs(out - ref_o).max() if out.size else 0.0
+    dl = np.abs(lse[fin] - ref_l[fin]).max() if fin.any() else 0.0
+    assert do <= TOL_O, f"{tag}: max|dO| = {do}"
+    assert dl <= TOL_LSE, f"{tag}: max|dLSE| = {dl}"
+    if not fin.all():
+        assert np.all(out[~fin] == 0), f"{tag}: rows with no visible key must be 0"
+    return do, dl
+
+
+# ------------------------------------------------------------- schedule --
+@pytest.mark.parametrize("seqlens,parts", [
+    ([64, 100], 256),
+    ([640, 192, 0, 65], 3),
+    ([1280], 4),
+    ([100, 1000, 1], 2),
+    ([0, 0, 0], 5),
+    ([1] * 300, 7),
+    ([131072, 1, 2, 3, 70000], 128),
+])
+def test_metadata_bit_exact(seqlens, parts):
+    _say(f"metadata {seqlens[:6]} parts={parts}")
+    seq = torch.tensor(seqlens, dtype=torch.int32, device="cuda:0")
+    sched, offs = api.get_metadata(seq, 1, 16, num_parts=parts)
+    torch.cuda.synchronize()
+    ref_s, ref_o = oracle_metadata(seqlens, parts)
+    assert np.array_equal(sched.cpu().numpy(), ref_s)
+    assert np.array_equal(offs.cpu().numpy(), ref_o)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_metadata_workloads_bit_exact(idx):
+    w = WORKLOADS[idx]
+    seqlens = workload_seqlens(idx)
+    seq = torch.tensor(seqlens, dtype=torch.int32, device="cuda:0")
+    sched, offs = api.get_metadata(seq, w.s_q, w.h_q)
+    torch.cuda.synchronize()
+    parts = sched.shape[0]
+    _say(f"metadata workload {idx} parts={parts}")
+    ref_s, ref_o = oracle_metadata(seqlens, parts)
+    assert np.array_equal(sched.cpu().numpy(), ref_s)
+    assert np.array_equal(offs.cpu().numpy(), ref_o)
+
+
+# --------------------------------------------------------- small parity --
+EDGE = [
+    # (s_q, h_q, seqlens, causal, dtype, num_parts)
+    (1, 16, (1, 2, 63, 64, 65), False, "bf16", None),
+    (1, 16, (127, 128, 129, 1000), False, "fp16", 3),
+    (2, 8, (1, 2, 63, 64, 65, 129), True, "bf16", 2),
+    (1, 1, (5, 300), False, "bf16", 1),
+    (1, 3, (300, 7), False, "fp16", 5),
+    (1, 64, (1, 64, 65, 200), False, "bf16", None),
+    (1, 64, (127, 640), False, "bf16", 4),
+    (2, 32, (1, 2, 65, 300), True, "fp16", 3),
+    (1, 128, (129, 1000), False, "bf16", 7),
+    (2, 128, (2, 3, 700), True, "fp16", 2),
+    (3, 40, (2, 129, 300), True, "bf16", 3),
+    (1, 17, (500, 64), False, "bf16", 6),
+]
+
+
+@pytest.mark.parametrize("s_q,h_q,seqlens,causal,dtype,parts", EDGE,
+                         ids=[f"sq{c[0]}_hq{c[1]}_{'c' if c[3] else 'n'}_{c[4]}_p{c[5]}" for c in EDGE])
+def test_small_parity(s_q, h_q, seqlens, causal, dtype, parts):
+    tag = f"small s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {dtype} parts={parts}"
+    _say(tag)
+    x = make_inputs(len(seqlens), s_q, h_q, dtype, seqlens=seqlens, causal=causal,
+                    seed=sum(seqlens) + h_q, poison=True, extra_pages=3)
+    out, lse, _ = run(x, parts)
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+    compare(out, lse, ref_o, ref_l, tag)
+
+
+def test_empty_request_and_masked_rows():
+    _say("empty request / fully masked causal rows")
+    x = make_inputs(3, 3, 16, "bf16", seqlens=(0, 1, 70), causal=True, seed=5, poison=True)
+    out, lse, _ = run(x, 2)
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, True)
+    compare(out, lse, ref_o, ref_l, "empty")
+    assert np.all(np.isneginf(lse[0])) and not out[0].any()
+
+
+def test_workload1_tiny_full():
+    _say("workload 1 (tiny), full comparison")
+    x = workload_inputs(1, poison=True)
+    out, lse, _ = run(x)
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, x.causal)
+    compare(out, lse, ref_o, ref_l, "workload 1")
+
+
+def test_strided_views():
+    _say("strided q / k_cache / out views")
+    x = make_inputs(3, 1, 64, "bf16", seqlens=(70, 200, 5), seed=9, poison=True)
+    dev = torch.device("cuda:0")
+    g = x.to(dev)
+    # q as a head-slice of a wider tensor, k_cache with padded slots
+    qbig = torch.zeros(3, 1, 80, 576, dtype=g.q.dtype, device=dev)
+    qbig[:, :, 8:72] = g.q
+    q = qbig[:, :, 8:72]
+    kbig = torch.zeros(g.k_cache.shape[0], 64, 1, 640, dtype=g.k_cache.dtype, device=dev)
+    kbig[..., :576] = g.k_cache
+    k = kbig[..., :576]
+    meta = api.get_metadata(g.cache_seqlens, 1, 64, num_parts=3)
+    bufs = api.DecodeBuffers(g.q, 3)
+    obig = torch.zeros(3, 1, 64, 520, dtype=g.q.dtype, device=dev)
+    bufs.out = obig[..., :512]
+    out, lse = api.mla_decode(q, k, g.block_table, g.cache_seqlens, g.softmax_scale, False,
+                              metadata=meta, buffers=bufs)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "strided")
+    assert not obig[..., 512:].any(), "padding of the output rows was written"
+
+
+# ------------------------------------------------------------ invariants --
+def test_page_permutation_is_bitwise_invariant():
+    _say("page permutation invariance")
+    x = make_inputs(4, 2, 64, "bf16", seqlens=(300, 64, 129, 1), causal=True, seed=17, extra_pages=2)
+    out1, lse1, _ = run(x, 5)
+    n = x.k_cache.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(3))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(n)
+    x.k_cache = x.k_cache[perm].contiguous()
+    used = x.block_table >= 0
+    x.block_table[used] = inv[x.block_table[used].long()].to(torch.int32)
+    out2, lse2, _ = run(x, 5)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_unused_slots_are_never_read_bitwise():
+    _say("garbage in unused slots and pages")
+    x = make_inputs(3, 1, 16, "fp16", seqlens=(70, 130, 3), seed=23, poison=True, extra_pages=4)
+    out1, lse1, _ = run(x, 4)
+    for b, nlen in enumerate((70, 130, 3)):
+        p = (nlen + 63) // 64
+        x.k_cache[int(x.block_table[b, p - 1]), nlen % 64:, 0, :] = -1000.0
+    used = set(int(v) for v in x.block_table.flatten().tolist() if v >= 0)
+    for page in range(x.k_cache.shape[0]):
+        if page not in used:
+            x.k_cache[page] = 777.0
+    out2, lse2, _ = run(x, 4)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_split_counts_agree(h_q):
+    _say(f"one partition vs many partitions h_q={h_q}")
+    x = make_inputs(5, 1, h_q, "bf16", seqlens=(900, 33, 2000, 640, 1), seed=31)
+    o1, l1, _ = run(x, 1)
+    o2, l2, m2 = run(x, 17)
+    assert (np.diff(m2[1]) > 1).any(), "expected some split requests"
+    assert np.abs(o1 - o2).max() <= 2e-3
+    assert np.abs(l1 - l2).max() <= 1e-4
+
+
+# ----------------------------------------------------- full-size samples --
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_workload_full_size_sampled(idx):
+    """Full-size workload in the launch configuration the benchmark uses;
+    the oracle checks a sample of requests (first, last, and the longest)."""
+    w = WORKLOADS[idx]
+    _say(f"workload {idx} {w.name} full size")
+    x = workload_inputs(idx)
+    out, lse, meta = run(x)
+    seqlens = x.cache_seqlens.tolist()
+    offs = meta[1]
+    split = [b for b in range(w.batch) if offs[b + 1] - offs[b] > 1]
+    whole = [b for b in range(w.batch) if offs[b + 1] - offs[b] == 1]
+    picks = sorted(set([0, w.batch - 1, int(np.argmax(seqlens))] + split[:1] + whole[:1]))
+    qf = x.q.double().numpy()
+    kf = x.k_cache.double().numpy()
+    for b in picks:
+        ref_o, ref_l = oracle_decode_rows(qf, kf, x.block_table, x.cache_seqlens, x.softmax_scale,
+                                          w.causal, b)
+        R = w.s_q * w.h_q
+        compare(out[b].reshape(R, 512), lse[b].reshape(R), ref_o, ref_l, f"workload {idx} request {b}")
+    assert np.isfinite(lse).all()
