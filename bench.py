@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of paged MLA decode on one MI355X.
+
+One step = the whole decode path over one batch: the tile schedule
+(mla_get_metadata), the split-KV attention kernel and the combine kernel.  The
+default workload is B=64 requests, s_q=1, h_q=128, every s_k=4096, bf16, 64-token
+pages reached through a shuffled block table (inputs seeded, synthetic).  Steps
+alternate between `--copies` independent KV caches (like successive layers), so
+one step's cache is not left in the last-level caches by the previous step.
+
+Prints ONE JSON line: whole-step TFLOP/s (algorithmic FLOPs / step time), the
+effective HBM GB/s, the roofline of the dominant kernel (split-KV) timed with
+HIP events on the stream it runs on, and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MLA decode TFLOP/s + effective HBM GB/s (bs64,h_q128,s_k4096) & roofline %"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E datasheet peak
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA
+D_K, D_V, PAGE = 576, 512, 64
+
+
+def algorithmic_counts(seqlens, batch, s_q, h_q, elem=2):
+    """FLOPs and bytes of one decode step, counted from the definition:
+    FLOPs = sum_b 2*h_q*s_q*s_k,b*(576+512); bytes = KV rows once (V lies inside
+    K) + Q + O + LSE + the block-table entries and lengths that are read."""
+    rows = s_q * h_q
+    flops = sum(2.0 * rows * n * (D_K + D_V) for n in seqlens)
+    kv = sum(n * D_K * elem for n in seqlens)
+    q = batch * rows * D_K * elem
+    o = batch * rows * D_V * elem
+    lse = batch * rows * 4
+    tables = sum((n + PAGE - 1) // PAGE for n in seqlens) * 4 + batch * 4
+    return flops, kv, q, o, lse, tables
+
+
+def cpu_baseline(inputs, seconds: float):
+    """The oracle, as it stands, over whole requests of the same workload until
+    `seconds` of CPU time have passed (at least one request)."""
+    import numpy as np
+    from oracle import oracle_decode_rows
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    qf = inputs.q.double().numpy()
+    kf = inputs.k_cache.double().numpy()
+    B, s_q, h_q, _ = qf.shape
+    seq = inputs.cache_seqlens.tolist()
+    done, flops, results = 0, 0.0, {}
+    t0 = time.perf_counter()
+    while True:
+        b = done % B
+        o, l = oracle_decode_rows(qf, kf, inputs.block_table, inputs.cache_seqlens,
+                                  inputs.softmax_scale, inputs.causal, b)
+        if b not in results:
+            results[b] = (o, l)
+        flops += 2.0 * s_q * h_q * seq[b] * (D_K + D_V)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} whole requests (request index mod {B}) of the same workload, fp64 NumPy, {dt:.1f} s",
+    }, results
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="1..5; 2 is the headline workload")
+    ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path is single-GPU; sharding is described in the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+        return 0
+
+    from mla_decode_attention_02_amd import api
+    from mla_decode_attention_02_amd.workloads import WORKLOADS, workload_inputs
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    host = workload_inputs(args.workload)
+    seqlens = host.cache_seqlens.tolist()
+    flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q)
+    step_bytes = kv + qb + ob + lseb + tb
+    splitkv_bytes = kv + qb + tb   # what every split-KV launch must read
+
+    # inputs resident in HBM before timing; `copies` independent KV caches
+    g = host.to(dev)
+    caches = [g.k_cache] + [g.k_cache.clone() for _ in range(max(1, args.copies) - 1)]
+    sched0, offs0 = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q)
+    num_parts = sched0.shape[0]
+    bufs = api.DecodeBuffers(g.q, num_parts)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        meta = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q, num_parts=num_parts)
+        k = caches[i % len(caches)]
+        if ev is not None:
+            ev[0].record()
+        api.mla_decode_splitkv(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+        if ev is not None:
+            ev[1].record()
+        api.mla_decode_combine(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    splitkv_ms = sorted(a.elapsed_time(b) for a, b in events)
+    splitkv_avg = sum(splitkv_ms) / len(splitkv_ms)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    ai = flops / step_bytes
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if ai < ridge:
+        ach = splitkv_bytes / (splitkv_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        ach = flops / (splitkv_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
+    roof["kernel_avg_us"] = round(splitkv_avg * 1e3, 2)
+    roof["kernel_p10_p90_us"] = [round(splitkv_ms[len(splitkv_ms) // 10] * 1e3, 2),
+                                 round(splitkv_ms[(9 * len(splitkv_ms)) // 10] * 1e3, 2)]
+    roof["algorithmic_bytes_per_launch"] = splitkv_bytes
+    roof["algorithmic_flops_per_launch"] = flops
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded randn q/KV, shuffled 64-token page table",
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
+                   "s_k": "4096" if args.workload == 2 else w.description, "d_k": D_K, "d_v": D_V,
+                   "page": PAGE, "causal": w.causal, "num_parts": num_parts, "kv_copies": len(caches)},
+        "effective_hbm_gbps": round(gbps, 1),
+        "effective_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        out = bufs.out.float().cpu().numpy()
+        lse = bufs.lse.cpu().numpy()
+        base, ref = cpu_baseline(host, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        R = w.s_q * w.h_q
+        do = max(float(np.abs(out[b].reshape(R, D_V) - o).max()) for b, (o, l) in ref.items())
+        dl = max(float(np.abs(lse[b].reshape(R) - l).max()) for b, (o, l) in ref.items())
+        result["parity_vs_oracle"] = {"requests": len(ref), "max_abs_dO": do, "max_abs_dLSE": dl}
+
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

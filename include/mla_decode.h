@@ -41,7 +41,8 @@
  *    behaviour): 0 <= cache_seqlens[b] <= max_pages_per_seq * 64; the entries
  *    block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages);
  *    `sched` / `split_offsets` were produced by mla_get_metadata from the same
- *    cache_seqlens with the same num_parts; cache contents are finite.
+ *    cache_seqlens with the same num_parts; cache contents are finite; the total
+ *    schedule cost sum_b (ceil(cache_seqlens[b] / 64) + 5) is below 2^31.
  *  - Thread safety: all entry points may be called concurrently; the error
  *    text is kept per thread.
  */
@@ -101,18 +102,20 @@ mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
 
 /*
  * Build the split-KV tile schedule on the device (one small kernel).
- * Every nonempty request b costs P_b + F, P_b = ceil(cache_seqlens[b] / 64),
- * F = MLA_FIXED_OVERHEAD; quota Q = ceil(sum of costs / num_parts) + F
- * (the page's formula).  Partitions are filled greedily in request order: a
- * request (or its remainder) that fits the remaining budget is taken whole,
- * otherwise the partition takes (budget - F) of its pages when that is positive
- * and closes.
- *   cache_seqlens  device int32 [batch], each >= 0.
+ * A nonempty request b costs c_b = P_b + F, P_b = ceil(cache_seqlens[b] / 64),
+ * F = MLA_FIXED_OVERHEAD; empty requests cost 0.  Costs are laid end to end in
+ * request order, request b starting at C_b with its F overhead units first, so
+ * page p of request b sits at position C_b + F + p.  With T = sum of costs and
+ * W = ceil(T / num_parts), partition k takes the pages whose positions fall in
+ * [k*W, (k+1)*W).  Each partition then costs at most W + F, the page's quota
+ * ceil(total / num_parts) + fixed overhead.
+ *   cache_seqlens  device int32 [batch], each >= 0, with
+ *                  sum_b (P_b + F) < 2^31.
  *   num_parts      >= 1 (normally from mla_get_metadata_shape).
  *   sched          device int32 [num_parts][8], written.  Row p =
  *                  (begin_req, begin_page, end_req, end_page, begin_split,
- *                   n_chunks, 0, 0): partition p covers request begin_req from
- *                  page begin_page, all requests strictly between, and request
+ *                   0, 0, 0): partition p covers request begin_req from page
+ *                  begin_page, all requests strictly between, and request
  *                  end_req up to page end_page (exclusive); begin_split is the
  *                  index of its first piece among the pieces of begin_req.
  *                  Empty partition: (0, 0, -1, 0, 0, 0, 0, 0).

@@ -1,75 +1,156 @@
 // Split-KV tile scheduler (page "FlashMLA: 高性能GPU注意力机制计算库 文件结构分析",
 // section "6. SM资源调度优化"): the work of all requests, in 64-token pages, is
 // spread over num_parts partitions with a per-partition quota of
-// ceil(total / num_parts) + F, where every piece of a request also costs the
-// fixed overhead F.  Partitions are filled greedily in request order; a request
-// that does not fit the remaining budget is cut after (budget - F) pages when
-// that is positive.  The schedule is a few hundred integer steps, so a single
-// lane builds it; the rest of the workgroup only computes the total cost.
+// ceil(total / num_parts) + F, where F is the fixed overhead every piece of a
+// request costs.
+//
+// Assignment rule: a nonempty request b costs c_b = pages_b + F.  The costs are
+// laid end to end in request order, request b starting at C_b with its F
+// overhead units first, so page p of request b sits at position C_b + F + p.
+// With T = sum of costs and W = ceil(T / num_parts), partition k takes the pages
+// whose positions fall in [k W, (k+1) W).  A partition pays at most one F that
+// lies outside its interval (a piece starting inside a request), so its cost
+// stays within the quota W + F.
+//
+// Everything is data-parallel: one workgroup scans the costs into C (LDS, or
+// split_offsets as scratch for very large batches), each thread then places one
+// or more partitions with two binary searches over C, and a second scan turns
+// the per-request piece counts into split_offsets.
 #include "mla_common.hpp"
 #include "mla_internal.h"
 
 namespace mla {
 
-__global__ __launch_bounds__(256) void metadata_kernel(const int32_t* __restrict__ seqlens, int batch,
-                                                       int num_parts, int F, int32_t* __restrict__ sched,
-                                                       int32_t* __restrict__ split_offsets) {
-  __shared__ long long partial[256];
-  const int tid = threadIdx.x;
-  long long acc = 0;
-  for (int b = tid; b < batch; b += blockDim.x) {
-    const int pages = (seqlens[b] + kPage - 1) / kPage;
-    if (pages > 0) acc += pages + F;
-  }
-  partial[tid] = acc;
-  for (int b = tid; b < batch; b += blockDim.x) split_offsets[b + 1] = 0;
-  __syncthreads();
-  if (tid != 0) return;
-  long long total = 0;
-  for (int i = 0; i < (int)blockDim.x; ++i) total += partial[i];
-  const long long quota = (total + num_parts - 1) / num_parts + F;
+constexpr int kMetaThreads = 256;
+constexpr int kMetaWaves = kMetaThreads / 64;
+constexpr int kMetaLdsBatch = 16384;   // requests whose start positions fit in LDS
 
-  int b = 0, pos = 0;   // next request, next page within it
-  for (int part = 0; part < num_parts; ++part) {
-    long long budget = quota;
-    int nchunks = 0, b0 = 0, p0 = 0, s0 = 0, b1 = -1, p1 = 0;
-    while (b < batch) {
-      const int pages = (seqlens[b] + kPage - 1) / kPage;
-      if (pages == 0) { ++b; pos = 0; continue; }
-      const long long need = (long long)(pages - pos) + F;
-      int lo = pos, hi;
-      bool done;
-      if (need <= budget) {
-        hi = pages;
-        budget -= need;
-        done = true;
-      } else {
-        const long long take = budget - F;
-        if (take <= 0) break;
-        hi = pos + (int)take;
-        done = false;
-      }
-      if (nchunks == 0) { b0 = b; p0 = lo; s0 = split_offsets[b + 1]; }
-      b1 = b; p1 = hi;
-      split_offsets[b + 1] += 1;
-      ++nchunks;
-      if (done) { ++b; pos = 0; } else { pos = hi; break; }
-    }
-    int32_t* row = sched + part * 8;
-    if (nchunks == 0) {
-      row[0] = 0; row[1] = 0; row[2] = -1; row[3] = 0; row[4] = 0; row[5] = 0;
-    } else {
-      row[0] = b0; row[1] = p0; row[2] = b1; row[3] = p1; row[4] = s0; row[5] = nchunks;
-    }
-    row[6] = 0; row[7] = 0;
+__device__ __forceinline__ int pages_of(int n) { return (n + kPage - 1) / kPage; }
+
+// Exclusive prefix sum of one value per thread across the workgroup.
+__device__ int block_exclusive_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
-  split_offsets[0] = 0;
-  for (int i = 0; i < batch; ++i) split_offsets[i + 1] += split_offsets[i];
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kMetaWaves; ++w) {
+    const int s = scratch[w];
+    before += (w < wave) ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  total = all;
+  return before + x - v;
+}
+
+// Largest request index b with C[b] <= pos (C[0] = 0 <= pos).  For pos < T this
+// is the nonempty request whose cost interval holds pos.
+__device__ __forceinline__ int find_request(const int* C, int batch, long long pos) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (C[mid] <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* __restrict__ seqlens, int batch,
+                                                                int num_parts, int F, int32_t* __restrict__ sched,
+                                                                int32_t* __restrict__ split_offsets) {
+  __shared__ int scan_s[kMetaWaves];
+  __shared__ int start_s[kMetaLdsBatch + 1];
+  const int tid = threadIdx.x;
+  const int per = (batch + kMetaThreads - 1) / kMetaThreads;
+  const int lo = min(batch, tid * per);
+  const int hi = min(batch, lo + per);
+  // start positions: LDS when they fit, else split_offsets (overwritten at the end)
+  int* C = batch <= kMetaLdsBatch ? start_s : split_offsets;
+
+  int local = 0;
+  for (int b = lo; b < hi; ++b) {
+    const int p = pages_of(seqlens[b]);
+    local += p > 0 ? p + F : 0;
+  }
+  int total;
+  const int first = block_exclusive_scan(local, scan_s, total);
+  {
+    int run = first;
+    for (int b = lo; b < hi; ++b) {
+      C[b] = run;
+      const int p = pages_of(seqlens[b]);
+      run += p > 0 ? p + F : 0;
+    }
+    if (tid == 0) C[batch] = total;
+  }
+  __syncthreads();
+  const int width = total > 0 ? (total + num_parts - 1) / num_parts : 1;
+
+  // pieces per request: how many partitions its page positions touch
+  auto pieces = [&](int start, int p) {
+    return p > 0 ? (start + F + p - 1) / width - (start + F) / width + 1 : 0;
+  };
+  int nsum = 0;
+  {
+    int run = first;
+    for (int b = lo; b < hi; ++b) {
+      const int p = pages_of(seqlens[b]);
+      nsum += pieces(run, p);
+      run += p > 0 ? p + F : 0;
+    }
+  }
+
+  // partitions
+  for (int k = tid; k < num_parts; k += kMetaThreads) {
+    const long long s = (long long)k * width;
+    const long long e = min((long long)total, s + width);
+    int row[8] = {0, 0, -1, 0, 0, 0, 0, 0};
+    if (s < total) {
+      const int b0 = find_request(C, batch, s);
+      const int c0 = C[b0];
+      if ((long long)c0 + F < e) {
+        const int p0 = s < (long long)c0 + F ? 0 : (int)(s - c0 - F);
+        long long last = e - 1;
+        int b1 = find_request(C, batch, last);
+        if (last < (long long)C[b1] + F) {      // part ends inside b1's overhead
+          last = (long long)C[b1] - 1;
+          b1 = find_request(C, batch, last);
+        }
+        row[0] = b0;
+        row[1] = p0;
+        row[2] = b1;
+        row[3] = (int)(last - C[b1] - F + 1);
+        row[4] = k - (c0 + F) / width;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sched[k * 8 + i] = row[i];
+  }
+
+  int nall;
+  const int sfirst = block_exclusive_scan(nsum, scan_s, nall);   // also orders the reads of C above
+  {
+    int run = sfirst, start = first;
+    for (int b = lo; b < hi; ++b) {
+      const int p = pages_of(seqlens[b]);
+      split_offsets[b] = run;
+      run += pieces(start, p);
+      start += p > 0 ? p + F : 0;
+    }
+    if (tid == 0) split_offsets[batch] = nall;
+  }
 }
 
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead,
                            int32_t* sched, int32_t* split_offsets, hipStream_t st) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(256), 0, st, seqlens, batch, num_parts,
+  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMetaThreads), 0, st, seqlens, batch, num_parts,
                      fixed_overhead, sched, split_offsets);
   return hipGetLastError();
 }

@@ -11,13 +11,15 @@ overhead paying for the extra cost of each piece a request is cut into.
 "辅助优化：可编程依赖启动与瓦片调度": a tile scheduler assigns requests and
 blocks to SMs for load balance; split pieces are merged by a combine kernel.
 
-The pages give the quota and the goal, not the assignment rule.  The reading
-used here (listed in the design notes): every nonempty request b costs
-P_b + F, P_b = ceil(n_b / 64) pages, F = fixed overhead; total T = sum of the
-costs; quota Q = ceil(T / num_parts) + F.  Partitions are filled greedily in
-request order: a request (or the rest of one) that fits in the remaining budget
-is taken whole; otherwise the partition takes (budget - F) of its pages, if that
-is positive, and closes.  Empty requests (n_b = 0) get no chunk and no split.
+The pages give the quota and the goal, not the assignment rule.  Reading used
+here (listed in the design notes): every nonempty request b costs c_b = P_b + F
+(P_b = ceil(n_b / 64) pages, F = fixed overhead), empty requests cost 0.  The
+costs are laid end to end on one line in request order, request b occupying
+[C_b, C_b + c_b) with its F overhead units first and then one unit per page, so
+page p of request b sits at position C_b + F + p.  With T = sum of the costs and
+Q' = ceil(T / num_parts), partition k takes every page whose position lies in
+[k Q', (k+1) Q').  A partition pays one extra F at most (for a piece that starts
+inside a request), so its cost never exceeds the quota Q' + F.
 """
 
 from __future__ import annotations
@@ -29,6 +31,7 @@ import numpy as np
 PAGE = 64
 FIXED_OVERHEAD = 5
 SCHED_FIELDS = 8
+EMPTY_PART = [0, 0, -1, 0, 0, 0, 0, 0]
 
 
 def _pages(n: int) -> int:
@@ -37,37 +40,26 @@ def _pages(n: int) -> int:
 
 def schedule_chunks(cache_seqlens: Sequence[int], num_parts: int,
                     fixed_overhead: int = FIXED_OVERHEAD) -> List[Tuple[int, int, int, int]]:
-    """Chunks (part, request, first_page, end_page) in schedule order."""
-    seq = [int(x) for x in cache_seqlens]
+    """Pieces (part, request, first_page, end_page), ordered by part then request."""
     if num_parts <= 0:
         raise ValueError("num_parts must be positive")
     F = int(fixed_overhead)
-    P = [_pages(n) for n in seq]
-    B = len(P)
+    P = [_pages(n) for n in cache_seqlens]
+    start = 0                       # C_b: where request b begins on the cost line
     total = sum(p + F for p in P if p > 0)
-    quota = -(-total // num_parts) + F
+    width = max(1, -(-total // num_parts))      # Q' = ceil(T / num_parts)
     chunks: List[Tuple[int, int, int, int]] = []
-    b, p = 0, 0
-    for part in range(num_parts):
-        budget = quota
-        while b < B:
-            if P[b] == 0:
-                b, p = b + 1, 0
-                continue
-            need = (P[b] - p) + F
-            if need <= budget:
-                chunks.append((part, b, p, P[b]))
-                budget -= need
-                b, p = b + 1, 0
+    for b, p_b in enumerate(P):
+        if p_b == 0:
+            continue
+        for page in range(p_b):
+            part = (start + F + page) // width
+            if chunks and chunks[-1][0] == part and chunks[-1][1] == b:
+                chunks[-1] = (part, b, chunks[-1][2], page + 1)
             else:
-                take = budget - F
-                if take > 0:
-                    chunks.append((part, b, p, p + take))
-                    p += take
-                break
-    # every page of every request is covered (quota argument; checked here)
-    if b != B:
-        raise AssertionError("schedule left work unassigned")
+                chunks.append((part, b, page, page + 1))
+        start += p_b + F
+    chunks.sort(key=lambda c: (c[0], c[1]))
     return chunks
 
 
@@ -75,34 +67,28 @@ def oracle_metadata(cache_seqlens: Sequence[int], num_parts: int,
                     fixed_overhead: int = FIXED_OVERHEAD):
     """Return (sched [num_parts, 8] int32, split_offsets [B+1] int32).
 
-    sched[part] = (begin_req, begin_page, end_req, end_page, begin_split,
-                   n_chunks, 0, 0)
+    sched[part] = (begin_req, begin_page, end_req, end_page, begin_split, 0, 0, 0)
       The part covers request begin_req from page begin_page, every request
       strictly between, and request end_req up to page end_page (exclusive);
       when begin_req == end_req the range is [begin_page, end_page).
-      begin_split is the index of the part's first chunk among the chunks of
-      begin_req; later requests of the part start at their split 0.
+      begin_split is the index of the part's first piece among the pieces of
+      begin_req; later requests of the part start at their piece 0.
       An empty part is (0, 0, -1, 0, 0, 0, 0, 0).
-    split_offsets = exclusive prefix sum of n_splits (chunks per request);
-      requests with no cached token have 0 splits.
+    split_offsets = exclusive prefix sum of n_splits (pieces per request);
+      requests with no cached token have 0 pieces.
     """
-    seq = [int(x) for x in cache_seqlens]
-    B = len(seq)
-    chunks = schedule_chunks(seq, num_parts, fixed_overhead)
-    n_splits = [0] * B
-    split_of_chunk = []
-    for (_, b, _, _) in chunks:
-        split_of_chunk.append(n_splits[b])
-        n_splits[b] += 1
-    sched = np.zeros((num_parts, SCHED_FIELDS), dtype=np.int32)
-    sched[:, 2] = -1
+    B = len(cache_seqlens)
+    chunks = schedule_chunks(cache_seqlens, num_parts, fixed_overhead)
+    pieces = [[] for _ in range(B)]
+    for ch in sorted(chunks, key=lambda c: (c[1], c[2])):
+        pieces[ch[1]].append(ch)
+    sched = np.tile(np.asarray(EMPTY_PART, dtype=np.int32), (num_parts, 1))
     by_part = {}
-    for idx, (part, b, lo, hi) in enumerate(chunks):
-        by_part.setdefault(part, []).append((idx, b, lo, hi))
+    for ch in chunks:
+        by_part.setdefault(ch[0], []).append(ch)
     for part, lst in by_part.items():
-        i0, b0, lo0, _ = lst[0]
-        _, b1, _, hi1 = lst[-1]
-        sched[part] = (b0, lo0, b1, hi1, split_of_chunk[i0], len(lst), 0, 0)
+        first, last = lst[0], lst[-1]
+        sched[part] = (first[1], first[2], last[1], last[3], pieces[first[1]].index(first), 0, 0, 0)
     offsets = np.zeros((B + 1,), dtype=np.int32)
-    offsets[1:] = np.cumsum(np.asarray(n_splits, dtype=np.int64)).astype(np.int32)
+    offsets[1:] = np.cumsum(np.asarray([len(x) for x in pieces], dtype=np.int64)).astype(np.int32)
     return sched, offsets

@@ -69,6 +69,8 @@ def compare(out, lse, ref_o, ref_l, tag):
     ([0, 0, 0], 5),
     ([1] * 300, 7),
     ([131072, 1, 2, 3, 70000], 128),
+    ([(i * 37) % 900 for i in range(9000)], 256),
+    ([(i * 53) % 300 for i in range(20000)], 256),   # beyond the scheduler's LDS staging
 ])
 def test_metadata_bit_exact(seqlens, parts):
     _say(f"metadata {seqlens[:6]} parts={parts}")
