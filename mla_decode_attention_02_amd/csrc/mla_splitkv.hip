@@ -85,10 +85,15 @@ __device__ __forceinline__ void for_each_chunk(const DecodeParams& p, F&& f) {
   }
 }
 
-__device__ __forceinline__ const char* page_ptr(const DecodeParams& p, int b, int pg) {
-  const int phys = ldu(p.block_table + (int64_t)b * p.bt_s + pg);
-  return (const char*)p.k + (int64_t)phys * p.k_s0 * 2;
+// Descriptor of physical page `phys` of the cache.
+__device__ __forceinline__ BufRsrc page_of(const DecodeParams& p, int phys, int page_bytes) {
+  return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0 * 2, page_bytes);
 }
+
+// Cache policy of page loads: the narrow kernel reads every page once; in the
+// wide kernel the row tiles of one request read the same pages and may meet in L2.
+constexpr int kNarrowAux = 2;
+constexpr int kWideAux = 0;
 
 // Page loop driver: pages [lo, hi) alternate between two LDS buffers.  The loop
 // is unrolled by two so that the buffer roles and the register stage a step
@@ -105,175 +110,258 @@ __device__ __forceinline__ void page_loop(int lo, int hi, MLA_LDS char* buf0, ML
 }
 
 // ------------------------------------------------------------------ wide --
+// 64 query rows per workgroup, 8 waves (two per SIMD) in two roles that work
+// on consecutive pages at the same time, so that on every SIMD the MFMAs and
+// LDS reads of one role overlap the softmax arithmetic and MFMAs of the other
+// (the MI355X counterpart of the seesaw schedule's two alternating
+// warpgroups):
+//   * score waves 0..3, (rg, kg) = (w >> 1, w & 1): S^T for query rows
+//     rg*32 .. +32 (two 16-row tiles, Q fragments in registers) and page keys
+//     kg*32 .. +32 of page j; each K fragment read from LDS feeds two MFMAs.
+//     The pair (rg, 0), (rg, 1) exchanges partial row maxima through LDS, then
+//     both write their probabilities P(j) (bf16/fp16) into the rope region of
+//     page j's buffer, whose K data they have finished reading.
+//   * output waves 4..7: O^T += V^T . P^T for 128 of the 512 output columns of
+//     all 64 rows, on page j-1 (V from its buffer, P(j-1) from its rope region).
+// Page j+1 is staged in registers (value rows by the output waves, rope rows
+// by the score waves) and written into the buffer of page j-1 once the output
+// waves are done with it.  Three workgroup
+// barriers per step: A (row maxima exchanged), C (page j-1 and P(j) done),
+// B (page j+1 stored).
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void splitkv_wide_kernel(DecodeParams p) {
+__global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char kbuf0_raw[kPageBytes];
   __shared__ __attribute__((aligned(1024))) char kbuf1_raw[kPageBytes];
-  __shared__ __attribute__((aligned(16))) char pbuf_raw[64 * 64 * 2];
-  __shared__ float alpha_s[64];
-  __shared__ float l_s[64];
+  __shared__ float alpha_s[2][64];
+  __shared__ float pmax_s[2][64];
+  __shared__ float l_s[2][64];
   __shared__ float m_s[64];
-  MLA_LDS char* kbuf0 = (MLA_LDS char*)kbuf0_raw;
-  MLA_LDS char* kbuf1 = (MLA_LDS char*)kbuf1_raw;
-  MLA_LDS char* pbuf = (MLA_LDS char*)pbuf_raw;
+  MLA_LDS char* const kbuf0 = (MLA_LDS char*)kbuf0_raw;
+  MLA_LDS char* const kbuf1 = (MLA_LDS char*)kbuf1_raw;
+  auto kbuf = [&](int i) { return (i & 1) ? kbuf1 : kbuf0; };
 
-  const int tid = threadIdx.x;
-  const int wave = wave_id(), lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int wave = wave_id();
   const int mrow0 = blockIdx.y * 64;
-  const int64_t row_bytes = p.k_s1 * 2;
+  const int row_bytes = (int)(p.k_s1 * 2);
+  const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
 
-  for_each_chunk(p, [&](const Chunk& c) {
-    // score role: query row qrow (lane li of this wave)
-    const int qrow = mrow0 + wave * 16 + li;
-    u32x4 qf[18];
-    load_q_frag<T>(p, c.b, qrow, g, qf);
-    const int cnt = qrow < p.rows ? visible_count(c.n, p.s_q, qrow / p.h_q, p.causal) : 0;
-    float m_run = -INFINITY;   // running max of this row, log2 units
-    float l_part = 0.f;        // this lane's share of the running sum
-    // output role: columns wave*128 .. +128 of all 64 rows, held transposed
-    f32x4 o[8][4];
+  // The role test is the outermost branch: each role walks the partition's
+  // chunks in its own loop, so the loop invariants of one role are not kept
+  // alive in the other.  Both loops meet at the same barriers.
+  if (wave < 4) {
+    // -------------------------------------------------------- score waves --
+    const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+    const int rg = wave >> 1, kg = wave & 1;
+    const int kvo = kg * 32 * 1024, kro = kg * 32 * 128;     // this wave's key half
+    for_each_chunk(p, [&](const Chunk& c) {
+      BlockWindow bw;
+      bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
+      const int n = c.hi - c.lo;
+      PageShare<2> st;
+      rope_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo), page_bytes), row_bytes, wave, lane);
+      rope_share_store(st, kbuf0, wave, lane);
+      u32x4 qf[2][18];
+      int cnt[2];
+      float m_run[2], l_part[2];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // lane-dependent parts of the LDS addresses
-    const int prow = wave * 16 + li;                       // P row written by this lane
-    const int vrow = 8 * g + (li >> 2);                    // value row (lo) of the transposed reads
-    const int vbase = vrow * 1024 + wave * 256 + (li & 1) * 8;
-    const int vkey = swz_v(vrow);                          // same for vrow + 32; vrow + 4 uses vkey ^ 8
-    const int vh = (li >> 1) & 1;
-
-    PageStage st;
-    stage_load(st, page_ptr(p, c.b, c.lo), row_bytes, wave, lane);
-    stage_store(st, kbuf0, wave, lane);
-    lds_barrier();
-    page_loop(c.lo, c.hi, kbuf0, kbuf1, [&](auto, MLA_LDS char* cur, MLA_LDS char* nxt, int pg) {
-      const bool more = pg + 1 < c.hi;
-      if (more) stage_load(st, page_ptr(p, c.b, pg + 1), row_bytes, wave, lane);
-
-      // S^T[key][row] over the 576-deep contraction; operand reads run one
-      // step ahead of the MFMAs
-      f32x4 s[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      u32x4 kf[2][4];
-      auto load_k = [&](auto ksc, u32x4(&dst)[4]) {
-        constexpr int ks = decltype(ksc)::value;
-        const int off = kchunk_off<ks>(li, g);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) dst[kt] = ld_lds16(cur + off + (ks < 16 ? kt * 16384 : kt * 2048));
-      };
-      load_k(std::integral_constant<int, 0>{}, kf[0]);
-      static_for<0, 18>([&](auto ksc) {
-        constexpr int ks = decltype(ksc)::value;
-        if constexpr (ks + 1 < 18) load_k(std::integral_constant<int, ks + 1>{}, kf[(ks + 1) & 1]);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) s[kt] = Dt<T>::mfma32(kf[ks & 1][kt], qf[ks], s[kt]);
-      });
-
-      // mask + online softmax for row qrow (lane holds keys kt*16 + 4g + r)
-      const int key0 = pg * kPage + 4 * g;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t = (key0 + kt * 16 + r < cnt) ? s[kt][r] * p.scale_log2 : -INFINITY;
-          s[kt][r] = t;
-          mx = fmaxf(mx, t);
-        }
-      mx = max_across_groups(mx);
-      float alpha = 1.f;
-      if (mx > m_run + kRescaleSlack) {
-        alpha = exp2f(m_run - mx);
-        m_run = mx;
+      for (int rt = 0; rt < 2; ++rt) {
+        const int qrow = mrow0 + rg * 32 + rt * 16 + li;
+        load_q_frag<T>(p, c.b, qrow, g, qf[rt]);
+        cnt[rt] = qrow < p.rows ? visible_count(c.n, p.s_q, qrow / p.h_q, p.causal) : 0;
+        m_run[rt] = -INFINITY;   // running max of the row, log2 units
+        l_part[rt] = 0.f;        // this lane's share of the running sum
       }
-      const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[kt][r] = __builtin_amdgcn_exp2f(s[kt][r] - msub);
-          rs += s[kt][r];
-        }
-        const u32x2 pk = {Dt<T>::pack2(s[kt][0], s[kt][1]), Dt<T>::pack2(s[kt][2], s[kt][3])};
-        const int chunk = kt * 2 + (g >> 1);
-        *(MLA_LDS u32x2*)(pbuf + prow * 128 + ((chunk ^ swz_r(prow)) << 4) + (g & 1) * 8) = pk;
-      }
-      l_part = l_part * alpha + rs;
-      if (g == 0) alpha_s[prow] = alpha;
       lds_barrier();
-
-      // O^T[col][row] += V^T . P^T for this wave's 128 columns
-      float a4[4];
+      for (int j = 0; j <= n; ++j) {
+        const bool more = j + 1 < n;
+        if (more) rope_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo + j + 1), page_bytes), row_bytes, wave, lane);
+        MLA_LDS char* cur = kbuf(j);
+        f32x4 s[2][2];
+        float mx[2] = {-INFINITY, -INFINITY};
+        if (j < n) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a4[rt] = alpha_s[rt * 16 + li];
-      const bool resc = (a4[0] != 1.f) | (a4[1] != 1.f) | (a4[2] != 1.f) | (a4[3] != 1.f);
-      if (__any(resc)) {
+          for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+            for (int kt = 0; kt < 2; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // S^T over the 576-deep contraction, operand reads one step ahead
+          u32x4 kf[2][2];
+          auto load_k = [&](auto ksc, u32x4(&dst)[2]) {
+            constexpr int ks = decltype(ksc)::value;
+            const int off = kchunk_off<ks>(li, g) + (ks < 16 ? kvo : kro);
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) o[ct][rt] *= a4[rt];
-      }
+            for (int kt = 0; kt < 2; ++kt) dst[kt] = ld_lds16(cur + off + (ks < 16 ? kt * 16384 : kt * 2048));
+          };
+          load_k(std::integral_constant<int, 0>{}, kf[0]);
+          static_for<0, 18>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
+            if constexpr (ks + 1 < 18) load_k(std::integral_constant<int, ks + 1>{}, kf[(ks + 1) & 1]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pf[4];
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int pr = rt * 16 + li;
-          pf[rt] = ld_lds16(pbuf + pr * 128 + (((ks * 4 + g) ^ swz_r(pr)) << 4));
+              for (int kt = 0; kt < 2; ++kt) s[rt][kt] = Dt<T>::mfma32(kf[ks & 1][kt], qf[rt][ks], s[rt][kt]);
+          });
+          // mask, partial row maxima over this wave's 32 keys
+          const int key0 = (c.lo + j) * kPage + kg * 32 + 4 * g;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float t = (key0 + kt * 16 + r < cnt[rt]) ? s[rt][kt][r] * p.scale_log2 : -INFINITY;
+                s[rt][kt][r] = t;
+                mx[rt] = fmaxf(mx[rt], t);
+              }
+            mx[rt] = max_across_groups(mx[rt]);
+            if (g == 0) pmax_s[kg][rg * 32 + rt * 16 + li] = mx[rt];
+          }
         }
-        u32x4 vf[2];
-        auto load_v = [&](int ct, u32x4& dst) {
-          const int x = ((2 * ct + vh) ^ vkey) << 4;
-          const u32x2 lo4 = ld_lds_tr(cur + vbase + ks * 32768 + x);
-          const u32x2 hi4 = ld_lds_tr(cur + vbase + ks * 32768 + 4096 + (x ^ 128));
-          dst = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
-        };
-        load_v(0, vf[0]);
+        lds_barrier();                                                      // A
+        if (j < n) {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          if (ct + 1 < 8) load_v(ct + 1, vf[(ct + 1) & 1]);
+          for (int rt = 0; rt < 2; ++rt) {
+            const int prow = rg * 32 + rt * 16 + li;
+            const float m_all = fmaxf(mx[rt], pmax_s[kg ^ 1][prow]);
+            float alpha = 1.f;
+            if (m_all > m_run[rt] + kRescaleSlack) {
+              alpha = exp2f(m_run[rt] - m_all);
+              m_run[rt] = m_all;
+            }
+            const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
+            float rs = 0.f;
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) o[ct][rt] = Dt<T>::mfma32(vf[ct & 1], pf[rt], o[ct][rt]);
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                s[rt][kt][r] = __builtin_amdgcn_exp2f(s[rt][kt][r] - msub);
+                rs += s[rt][kt][r];
+              }
+              // P(j) into the rope region of page j's buffer, as rows of 64 keys
+              const u32x2 pk = {Dt<T>::pack2(s[rt][kt][0], s[rt][kt][1]), Dt<T>::pack2(s[rt][kt][2], s[rt][kt][3])};
+              const int chunk = kg * 4 + kt * 2 + (g >> 1);
+              *(MLA_LDS u32x2*)(cur + kRopeOff + prow * 128 + ((chunk ^ swz_r(prow)) << 4) + (g & 1) * 8) = pk;
+            }
+            l_part[rt] = l_part[rt] * alpha + rs;
+            if (kg == 0 && g == 0) alpha_s[j & 1][prow] = alpha;
+          }
+        }
+        lds_barrier();                                                      // C
+        if (more) rope_share_store(st, kbuf(j + 1), wave, lane);
+        lds_barrier();                                                      // B
+      }
+      // row sums of both key halves and the maxima for the output waves
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float lw = sum_across_groups(l_part[rt]);
+        const int prow = rg * 32 + rt * 16 + li;
+        if (g == 0) {
+          l_s[kg][prow] = lw;
+          if (kg == 0) m_s[prow] = m_run[rt];
         }
       }
-      if (more) stage_store(st, nxt, wave, lane);
-      lds_barrier();
+      lds_barrier();                                                        // E
+      lds_barrier();                                                        // F
     });
-
-    // epilogue: normalise, write the final output or an fp32 partial
-    const float l_row = sum_across_groups(l_part);
-    if (g == 0) {
-      l_s[prow] = l_row;
-      m_s[prow] = m_run;
-    }
-    lds_barrier();
+  } else {
+    // ------------------------------------------------------- output waves --
+    const int cw = wave - 4;                                  // columns cw*128 .. +128
+    for_each_chunk(p, [&](const Chunk& c) {
+      const int lane = threadIdx.x & 63;
+      BlockWindow bw;
+      bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
+      const int n = c.hi - c.lo;
+      PageShare<16> st;
+      value_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo), page_bytes), row_bytes, cw, lane);
+      value_share_store(st, kbuf0, cw, lane);
+      f32x4 o[8][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int rl = rt * 16 + li;
-      const int row = mrow0 + rl;
-      if (row >= p.rows) continue;
-      const float l = l_s[rl];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const float lse = lse_of(m_s[rl], l);
-      if (c.nsplit == 1) {
+      for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-          store_out4<T>(p, c.b, row, wave * 128 + ct * 16 + 4 * g, o[ct][rt] * inv);
-        if (wave == 0 && g == 0) p.lse[(int64_t)c.b * p.rows + row] = lse;
-      } else {
-        const int64_t slot = c.slot0 + c.split;
-        float* dst = p.part_o + (slot * p.rows + row) * kDV + wave * 128 + 4 * g;
+        for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lds_barrier();
+      for (int j = 0; j <= n; ++j) {
+        // Lane-dependent address parts are rebuilt every step from an opaque
+        // copy of the lane index: cheaper than pinning ~48 precomputed
+        // addresses in registers across the loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int gg = ln >> 4, ll = ln & 15;
+        const int vrow = 8 * gg + (ll >> 2);                 // value row (lo) of the transposed reads
+        const int vbase = vrow * 1024 + cw * 256 + (ll & 1) * 8;
+        const int vkey = swz_v(vrow);                        // same for vrow + 32; vrow + 4 uses vkey ^ 8
+        const int vh = (ll >> 1) & 1;
+        const bool more = j + 1 < n;
+        if (more) value_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo + j + 1), page_bytes), row_bytes, cw, ln);
+        MLA_LDS char* prv = kbuf(j + 1);                     // page j-1
+        auto load_v = [&](int ks, int ct) {
+          const int x = ((2 * ct + vh) ^ vkey) << 4;
+          const u32x2 lo4 = ld_lds_tr(prv + vbase + ks * 32768 + x);
+          const u32x2 hi4 = ld_lds_tr(prv + vbase + ks * 32768 + 4096 + (x ^ 128));
+          return u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+        };
+        // O^T[col][row] += V^T . P^T over keys ks*32 .. +32 of page j-1
+        auto pv_half = [&](int ks) {
+          u32x4 pf[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) *(f32x4*)(dst + ct * 16) = o[ct][rt] * inv;
-        if (wave == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+          for (int rt = 0; rt < 4; ++rt) {
+            const int pr = rt * 16 + ll;
+            pf[rt] = ld_lds16(prv + kRopeOff + pr * 128 + (((ks * 4 + gg) ^ swz_r(pr)) << 4));
+          }
+          u32x4 vf[2];
+          vf[0] = load_v(ks, 0);
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) {
+            if (ct + 1 < 8) vf[(ct + 1) & 1] = load_v(ks, ct + 1);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) o[ct][rt] = Dt<T>::mfma32(vf[ct & 1], pf[rt], o[ct][rt]);
+          }
+        };
+        if (j >= 1) {
+          float a4[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) a4[rt] = alpha_s[(j - 1) & 1][rt * 16 + ll];
+          const bool resc = (a4[0] != 1.f) | (a4[1] != 1.f) | (a4[2] != 1.f) | (a4[3] != 1.f);
+          if (__any(resc)) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+              for (int rt = 0; rt < 4; ++rt) o[ct][rt] *= a4[rt];
+          }
+          pv_half(0);
+        }
+        lds_barrier();                                                      // A
+        if (j >= 1) pv_half(1);
+        lds_barrier();                                                      // C
+        if (more) value_share_store(st, kbuf(j + 1), cw, ln);
+        lds_barrier();                                                      // B
       }
-    }
-    lds_barrier();
-  });
+      lds_barrier();                                                        // E
+      // epilogue: normalise, write the final output or an fp32 partial
+      const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int rl = rt * 16 + li;
+        const int row = mrow0 + rl;
+        if (row >= p.rows) continue;
+        const float l = l_s[0][rl] + l_s[1][rl];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float lse = lse_of(m_s[rl], l);
+        if (c.nsplit == 1) {
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+            store_out4<T>(p, c.b, row, cw * 128 + ct * 16 + 4 * g, o[ct][rt] * inv);
+          if (cw == 0 && g == 0) p.lse[(int64_t)c.b * p.rows + row] = lse;
+        } else {
+          const int64_t slot = c.slot0 + c.split;
+          float* dst = p.part_o + (slot * p.rows + row) * kDV + cw * 128 + 4 * g;
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) *(f32x4*)(dst + ct * 16) = o[ct][rt] * inv;
+          if (cw == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+        }
+      }
+      lds_barrier();                                                        // F
+    });
+  }
 }
 
 // ---------------------------------------------------------------- narrow --
@@ -290,9 +378,12 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
 
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int64_t row_bytes = p.k_s1 * 2;
+  const int row_bytes = (int)(p.k_s1 * 2);
+  const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
 
   for_each_chunk(p, [&](const Chunk& c) {
+    BlockWindow bw;
+    bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
     u32x4 qf[18];
     load_q_frag<T>(p, c.b, li, g, qf);
     const int cnt = li < p.rows ? visible_count(c.n, p.s_q, li / p.h_q, p.causal) : 0;
@@ -309,13 +400,13 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
 
     // two pages in flight in registers while a third is read from LDS
     PageStage st[2];
-    stage_load(st[0], page_ptr(p, c.b, c.lo), row_bytes, wave, lane);
-    if (c.lo + 1 < c.hi) stage_load(st[1], page_ptr(p, c.b, c.lo + 1), row_bytes, wave, lane);
+    stage_load<kNarrowAux>(st[0], page_of(p, bw.phys(c.lo), page_bytes), row_bytes, wave, lane);
+    if (c.lo + 1 < c.hi) stage_load<kNarrowAux>(st[1], page_of(p, bw.phys(c.lo + 1), page_bytes), row_bytes, wave, lane);
     stage_store(st[0], kbuf0, wave, lane);
     lds_barrier();
     page_loop(c.lo, c.hi, kbuf0, kbuf1, [&](auto par, MLA_LDS char* cur, MLA_LDS char* nxt, int pg) {
       constexpr int P = decltype(par)::value;   // st[P] held page pg, st[P ^ 1] holds pg + 1
-      if (pg + 2 < c.hi) stage_load(st[P], page_ptr(p, c.b, pg + 2), row_bytes, wave, lane);
+      if (pg + 2 < c.hi) stage_load<kNarrowAux>(st[P], page_of(p, bw.phys(pg + 2), page_bytes), row_bytes, wave, lane);
 
       // S^T for keys wave*16 .. +16 of the page, all 16 rows; operand reads
       // run two steps ahead of the MFMAs
@@ -430,7 +521,7 @@ static hipError_t launch_splitkv_t(const DecodeParams& p, int m_blocks, bool nar
   if (narrow) {
     hipLaunchKernelGGL(splitkv_narrow_kernel<T>, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL(splitkv_wide_kernel<T>, dim3(p.num_parts, m_blocks), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(splitkv_wide_kernel<T>, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
   }
   return hipGetLastError();
 }
