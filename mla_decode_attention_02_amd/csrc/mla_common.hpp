@@ -98,13 +98,20 @@ template <> struct Dt<_Float16> {
 // LDS image of one page (73728 bytes):
 //   value region  [64 rows][64 chunks of 16 B]  bytes      0 .. 65535  (columns 0..511)
 //   rope region   [64 rows][ 8 chunks of 16 B]  bytes  65536 .. 73727  (columns 512..575)
-// Chunks are XOR-swizzled within a row.  In the value region the key is a 4-bit
-// function of the row, so that 16 consecutive rows at one chunk (score reads)
-// and 4 consecutive rows x 2 chunks (transposed value reads) each hit distinct
-// bank groups; the rope region uses a 3-bit key for its 128-byte rows.
+// Chunks are XOR-swizzled within a row so that the reads of the kernels hit
+// the 64 four-byte LDS banks without conflicts.  On gfx950 a 16-byte-per-lane
+// LDS read is served 16 lanes per clock, in the lane sets {0-7, 24-31},
+// {8-15, 16-23}, {32-39, 56-63} and {40-47, 48-55} (measured); a set is
+// conflict-free when its 16 accesses fall into 16 distinct 16-byte bank
+// groups (address bits 4..7).  The score reads of a 16-row tile put rows
+// r and r+8 of lane groups g and g^1 into one set, so the value-region key is
+// (row & 7) << 1: rows 0..7 land on even groups, and g^1 moves rows 8..15 to
+// the odd ones.  The same key keeps the transposed value reads (4 rows x 2
+// chunks per 16 lanes) at their full rate; the rope region uses a 3-bit key
+// for its 128-byte rows.
 constexpr int kRopeOff = 64 * 1024;
 
-__device__ __forceinline__ int swz_v(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
 __device__ __forceinline__ int swz_r(int row) { return (row >> 1) & 7; }
 
 // Byte offset of the 16-byte chunk holding columns 8c..8c+7 (c < 64) of `row`.
@@ -187,7 +194,7 @@ template <int kAux>
 __device__ __forceinline__ void stage_load(PageStage& st, BufRsrc page, int row_bytes, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int key = ((j & 7) << 1) | ((j >> 3) & 1);       // == swz_v(16 * wave + j)
+    const int key = (j & 7) << 1;                          // == swz_v(16 * wave + j)
     st.v[j] = buf_load16<kAux>(page, (lane ^ key) << 4, (wave * 16 + j) * row_bytes);
   }
 #pragma unroll
@@ -225,41 +232,74 @@ struct BlockWindow {
   }
 };
 
-// Split staging of one page between the two roles of an 8-wave workgroup:
-// output wave w (0..3) stages value rows 16w .. 16w+15 (16 KiB), score wave w
-// stages rope blocks 2w, 2w+1 (rope rows 16w .. 16w+15, 2 KiB).
+// ------------------------------------------------------------ half pages --
+// LDS image of half a page (32 consecutive tokens, 36864 bytes), filled by
+// direct HBM -> LDS loads (LDS-DMA, no register staging):
+//   value region  [32 rows][64 chunks of 16 B]  bytes      0 .. 32767
+//   rope region   [32 rows][ 8 chunks of 16 B]  bytes  32768 .. 36863
+// with the same in-row swizzles as the full-page image.  Once the score pass
+// over a half page is done, its rope region is reused for the probabilities
+// P[64 rows][32 keys], stored key-group major: the 16 bytes of keys 8c..8c+7
+// of row r at 1024 c + 16 r, so that each 16-lane group of an operand read
+// covers 256 contiguous bytes.
+constexpr int kHalfRows = 32;
+constexpr int kHalfBytes = kHalfRows * kDK * 2;     // 36864
+constexpr int kHalfRopeOff = kHalfRows * 1024;      // 32768
+
+// Score-operand chunk ks*4 + g of half-page row `row` (ks compile-time).
+template <int KS>
+__device__ __forceinline__ int hchunk_off(int row, int g) {
+  if constexpr (KS < 16) {
+    return row * 1024 + (KS >> 2) * 256 + ((((KS & 3) * 4 + g) ^ swz_v(row)) << 4);
+  } else {
+    return kHalfRopeOff + row * 128 + ((((KS - 16) * 4 + g) ^ swz_r(row)) << 4);
+  }
+}
+
+// Byte offset of 16-byte chunk c (keys 8c .. 8c+7) of row `row` of the P tile.
+__device__ __forceinline__ int pchunk_off(int row, int c) { return kHalfRopeOff + c * 1024 + row * 16; }
+
+// One LDS-DMA instruction: every lane moves 16 bytes from the page at
+// (voff + soff) to LDS address dst + 16 * lane.
+template <int kAux>
+__device__ __forceinline__ void dma16(BufRsrc page, MLA_LDS char* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(page, (MLA_LDS void*)dst, 16, voff, soff, 0, kAux);
+}
+
+// Value rows r0 .. r0+3 of half page `half` (0/1) of a page into half buffer
+// `hb`: one 1 KiB row per instruction, lane l fetching the chunk that belongs
+// in slot l of its row, i.e. chunk l ^ swz_v(row).
+template <int kAux>
+__device__ __forceinline__ void dma_value_rows4(BufRsrc page, MLA_LDS char* hb, int half, int r0, int row_bytes,
+                                                int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = r0 + j;
+    const int key = (r & 7) << 1;                      // == swz_v(r), uniform
+    dma16<kAux>(page, hb + r * 1024, (lane ^ key) << 4, (half * kHalfRows + r) * row_bytes);
+  }
+}
+
+// Rope rows 8i .. 8i+7 of half page `half` (one instruction; lane l takes row
+// 8i + l/8, slot l%8).
+template <int kAux>
+__device__ __forceinline__ void dma_rope_rows8(BufRsrc page, MLA_LDS char* hb, int half, int i, int row_bytes,
+                                               int lane) {
+  const int r = i * 8 + (lane >> 3);
+  const int voff = (lane >> 3) * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
+  dma16<kAux>(page, hb + kHalfRopeOff + i * 1024, voff, (half * kHalfRows + i * 8) * row_bytes);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (its older LDS-DMA loads have landed), then a workgroup barrier that also
+// orders LDS accesses.  The vmcnt wait is the builtin, so that the compiler's
+// own wait placement knows which loads are still in flight after it.
 template <int N>
-struct PageShare {
-  u32x4 v[N];
-};
-
-template <int kAux>
-__device__ __forceinline__ void value_share_load(PageShare<16>& st, BufRsrc page, int row_bytes, int w, int lane) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int key = ((j & 7) << 1) | ((j >> 3) & 1);       // == swz_v(16 * w + j)
-    st.v[j] = buf_load16<kAux>(page, (lane ^ key) << 4, (w * 16 + j) * row_bytes);
-  }
-}
-
-__device__ __forceinline__ void value_share_store(const PageShare<16>& st, MLA_LDS char* buf, int w, int lane) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) *(MLA_LDS u32x4*)(buf + (w * 16 + j) * 1024 + lane * 16) = st.v[j];
-}
-
-template <int kAux>
-__device__ __forceinline__ void rope_share_load(PageShare<2>& st, BufRsrc page, int row_bytes, int w, int lane) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (w * 2 + i) * 8 + (lane >> 3);
-    const int voff = (lane >> 3) * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
-    st.v[i] = buf_load16<kAux>(page, voff, (w * 2 + i) * 8 * row_bytes);
-  }
-}
-
-__device__ __forceinline__ void rope_share_store(const PageShare<2>& st, MLA_LDS char* buf, int w, int lane) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) *(MLA_LDS u32x4*)(buf + kRopeOff + (w * 2 + i) * 1024 + lane * 16) = st.v[i];
+__device__ __forceinline__ void dma_barrier() {
+  static_assert(N >= 0 && N <= 15, "vmcnt immediate");
+  // s_waitcnt fields: vmcnt [3:0], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15 = no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Write a staged page into an LDS page buffer (contiguous 1 KiB per instruction).

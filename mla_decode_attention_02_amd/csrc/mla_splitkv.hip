@@ -111,55 +111,80 @@ __device__ __forceinline__ void page_loop(int lo, int hi, MLA_LDS char* buf0, ML
 
 // ------------------------------------------------------------------ wide --
 // 64 query rows per workgroup, 8 waves (two per SIMD) in two roles that work
-// on consecutive pages at the same time, so that on every SIMD the MFMAs and
-// LDS reads of one role overlap the softmax arithmetic and MFMAs of the other
-// (the MI355X counterpart of the seesaw schedule's two alternating
+// on consecutive half pages (32 keys) at the same time, so that on every SIMD
+// the MFMAs and LDS reads of one role overlap the softmax arithmetic of the
+// other (the MI355X counterpart of the seesaw schedule's two alternating
 // warpgroups):
 //   * score waves 0..3, (rg, kg) = (w >> 1, w & 1): S^T for query rows
-//     rg*32 .. +32 (two 16-row tiles, Q fragments in registers) and page keys
-//     kg*32 .. +32 of page j; each K fragment read from LDS feeds two MFMAs.
-//     The pair (rg, 0), (rg, 1) exchanges partial row maxima through LDS, then
-//     both write their probabilities P(j) (bf16/fp16) into the rope region of
-//     page j's buffer, whose K data they have finished reading.
+//     rg*32 .. +32 (two 16-row tiles, Q fragments in registers) and keys
+//     kg*16 .. +16 of half page h; each K fragment read from LDS feeds two
+//     MFMAs.  The pair (rg, 0), (rg, 1) exchanges partial row maxima through
+//     LDS, then both write their probabilities P(h) into the rope region of
+//     half page h's buffer, whose K data every score wave has read by then.
 //   * output waves 4..7: O^T += V^T . P^T for 128 of the 512 output columns of
-//     all 64 rows, on page j-1 (V from its buffer, P(j-1) from its rope region).
-// Page j+1 is staged in registers (value rows by the output waves, rope rows
-// by the score waves) and written into the buffer of page j-1 once the output
-// waves are done with it.  Three workgroup
-// barriers per step: A (row maxima exchanged), C (page j-1 and P(j) done),
-// B (page j+1 stored).
+//     all 64 rows, on half page h-1 (V from its buffer, P(h-1) from its rope
+//     region).
+// Half pages stream HBM -> LDS by direct (LDS-DMA) loads into four buffers:
+// at step h, h is scored, h-1 accumulated, and h+1 and h+2 are in flight, so
+// a load has two steps to land and no registers hold data in transit.  The
+// loads of a half page are spread over all eight waves.  Two workgroup
+// barriers per step: A (row maxima exchanged, K of h read) and B (P(h)
+// written, h-1 consumed, h+1 landed).  Buffers are named at compile time
+// (the step loop is unrolled by four) so that the compiler can tell the LDS
+// reads of one buffer from the loads in flight into another.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char kbuf0_raw[kPageBytes];
-  __shared__ __attribute__((aligned(1024))) char kbuf1_raw[kPageBytes];
+  __shared__ __attribute__((aligned(1024))) char hb0_raw[kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char hb1_raw[kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char hb2_raw[kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char hb3_raw[kHalfBytes];
   __shared__ float alpha_s[2][64];
   __shared__ float pmax_s[2][64];
   __shared__ float l_s[2][64];
   __shared__ float m_s[64];
-  MLA_LDS char* const kbuf0 = (MLA_LDS char*)kbuf0_raw;
-  MLA_LDS char* const kbuf1 = (MLA_LDS char*)kbuf1_raw;
-  auto kbuf = [&](int i) { return (i & 1) ? kbuf1 : kbuf0; };
+  auto hbuf = [&](auto ic) -> MLA_LDS char* {
+    constexpr int i = decltype(ic)::value & 3;
+    if constexpr (i == 0) return (MLA_LDS char*)hb0_raw;
+    else if constexpr (i == 1) return (MLA_LDS char*)hb1_raw;
+    else if constexpr (i == 2) return (MLA_LDS char*)hb2_raw;
+    else return (MLA_LDS char*)hb3_raw;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
   const int mrow0 = blockIdx.y * 64;
   const int row_bytes = (int)(p.k_s1 * 2);
   const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
+
+  // Descriptor for the loads of half page hh of a chunk.  Every step issues
+  // its share of loads, also when no half page is left: those use an empty
+  // descriptor (every lane out of range, no memory access), so that each wave
+  // has the same number of loads in flight at every barrier.
+  auto dma_page = [&](BlockWindow& bw, const Chunk& c, int hh, int nh) {
+    const bool real = hh < nh;
+    return page_of(p, real ? bw.phys(c.lo + (hh >> 1)) : 0, real ? page_bytes : 0);
+  };
+  // Half pages of a chunk: its pages, less a last half that lies wholly past
+  // the end of the request.
+  auto half_pages = [&](const Chunk& c) {
+    const int end = min(c.n, c.hi * kPage);
+    return (end - c.lo * kPage + kHalfRows - 1) / kHalfRows;
+  };
 
   // The role test is the outermost branch: each role walks the partition's
   // chunks in its own loop, so the loop invariants of one role are not kept
   // alive in the other.  Both loops meet at the same barriers.
   if (wave < 4) {
     // -------------------------------------------------------- score waves --
-    const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+    const int g = lane >> 4, li = lane & 15;
     const int rg = wave >> 1, kg = wave & 1;
-    const int kvo = kg * 32 * 1024, kro = kg * 32 * 128;     // this wave's key half
+    const int krow = kg * 16 + li;                            // K row read by this lane
     for_each_chunk(p, [&](const Chunk& c) {
       BlockWindow bw;
       bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
-      const int n = c.hi - c.lo;
-      PageShare<2> st;
-      rope_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo), page_bytes), row_bytes, wave, lane);
-      rope_share_store(st, kbuf0, wave, lane);
+      const int nh = half_pages(c);
       u32x4 qf[2][18];
       int cnt[2];
       float m_run[2], l_part[2];
@@ -171,53 +196,51 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         m_run[rt] = -INFINITY;   // running max of the row, log2 units
         l_part[rt] = 0.f;        // this lane's share of the running sum
       }
-      lds_barrier();
-      for (int j = 0; j <= n; ++j) {
-        const bool more = j + 1 < n;
-        if (more) rope_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo + j + 1), page_bytes), row_bytes, wave, lane);
-        MLA_LDS char* cur = kbuf(j);
-        f32x4 s[2][2];
+      // this wave's share of a half page: value rows 4w .. 4w+3, rope block w
+      auto issue = [&](auto ic, int hh) {
+        const BufRsrc pg = dma_page(bw, c, hh, nh);
+        dma_value_rows4<kWideAux>(pg, hbuf(ic), hh & 1, 4 * wave, row_bytes, lane);
+        dma_rope_rows8<kWideAux>(pg, hbuf(ic), hh & 1, wave, row_bytes, lane);
+      };
+      issue(I0{}, 0);
+      issue(I1{}, 1);
+      dma_barrier<5>();
+
+      auto step = [&](auto Hc, int h) {
+        constexpr int H = decltype(Hc)::value;
+        MLA_LDS char* cur = hbuf(Hc);
+        issue(std::integral_constant<int, H + 2>{}, h + 2);
+        f32x4 s[2];
         float mx[2] = {-INFINITY, -INFINITY};
-        if (j < n) {
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // S^T over the 576-deep contraction, operand reads one step ahead
-          u32x4 kf[2][2];
-          auto load_k = [&](auto ksc, u32x4(&dst)[2]) {
-            constexpr int ks = decltype(ksc)::value;
-            const int off = kchunk_off<ks>(li, g) + (ks < 16 ? kvo : kro);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) dst[kt] = ld_lds16(cur + off + (ks < 16 ? kt * 16384 : kt * 2048));
-          };
-          load_k(std::integral_constant<int, 0>{}, kf[0]);
+        if (h < nh) {
+          s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+          s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // S^T over the 576-deep contraction, operand reads two steps ahead
+          u32x4 kf[3];
+          kf[0] = ld_lds16(cur + hchunk_off<0>(krow, g));
+          kf[1] = ld_lds16(cur + hchunk_off<1>(krow, g));
           static_for<0, 18>([&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
-            if constexpr (ks + 1 < 18) load_k(std::integral_constant<int, ks + 1>{}, kf[(ks + 1) & 1]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-              for (int kt = 0; kt < 2; ++kt) s[rt][kt] = Dt<T>::mfma32(kf[ks & 1][kt], qf[rt][ks], s[rt][kt]);
+            if constexpr (ks + 2 < 18) kf[(ks + 2) % 3] = ld_lds16(cur + hchunk_off<ks + 2>(krow, g));
+            s[0] = Dt<T>::mfma32(kf[ks % 3], qf[0][ks], s[0]);
+            s[1] = Dt<T>::mfma32(kf[ks % 3], qf[1][ks], s[1]);
           });
-          // mask, partial row maxima over this wave's 32 keys
-          const int key0 = (c.lo + j) * kPage + kg * 32 + 4 * g;
+          // mask, partial row maxima over this wave's 16 keys
+          const int key0 = (2 * c.lo + h) * kHalfRows + kg * 16 + 4 * g;
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float t = (key0 + kt * 16 + r < cnt[rt]) ? s[rt][kt][r] * p.scale_log2 : -INFINITY;
-                s[rt][kt][r] = t;
-                mx[rt] = fmaxf(mx[rt], t);
-              }
+            for (int r = 0; r < 4; ++r) {
+              const float t = (key0 + r < cnt[rt]) ? s[rt][r] * p.scale_log2 : -INFINITY;
+              s[rt][r] = t;
+              mx[rt] = fmaxf(mx[rt], t);
+            }
             mx[rt] = max_across_groups(mx[rt]);
             if (g == 0) pmax_s[kg][rg * 32 + rt * 16 + li] = mx[rt];
           }
         }
         lds_barrier();                                                      // A
-        if (j < n) {
+        if (h < nh) {
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
             const int prow = rg * 32 + rt * 16 + li;
@@ -230,24 +253,23 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
             const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
             float rs = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                s[rt][kt][r] = __builtin_amdgcn_exp2f(s[rt][kt][r] - msub);
-                rs += s[rt][kt][r];
-              }
-              // P(j) into the rope region of page j's buffer, as rows of 64 keys
-              const u32x2 pk = {Dt<T>::pack2(s[rt][kt][0], s[rt][kt][1]), Dt<T>::pack2(s[rt][kt][2], s[rt][kt][3])};
-              const int chunk = kg * 4 + kt * 2 + (g >> 1);
-              *(MLA_LDS u32x2*)(cur + kRopeOff + prow * 128 + ((chunk ^ swz_r(prow)) << 4) + (g & 1) * 8) = pk;
+            for (int r = 0; r < 4; ++r) {
+              s[rt][r] = __builtin_amdgcn_exp2f(s[rt][r] - msub);
+              rs += s[rt][r];
             }
+            const u32x2 pk = {Dt<T>::pack2(s[rt][0], s[rt][1]), Dt<T>::pack2(s[rt][2], s[rt][3])};
+            *(MLA_LDS u32x2*)(cur + pchunk_off(prow, kg * 2 + (g >> 1)) + (g & 1) * 8) = pk;
             l_part[rt] = l_part[rt] * alpha + rs;
-            if (kg == 0 && g == 0) alpha_s[j & 1][prow] = alpha;
+            if (kg == 0 && g == 0) alpha_s[h & 1][prow] = alpha;
           }
         }
-        lds_barrier();                                                      // C
-        if (more) rope_share_store(st, kbuf(j + 1), wave, lane);
-        lds_barrier();                                                      // B
+        dma_barrier<5>();                                                   // B
+      };
+      for (int h0 = 0; h0 <= nh; h0 += 4) {
+        static_for<0, 4>([&](auto Hc) {
+          const int h = h0 + decltype(Hc)::value;
+          if (h <= nh) step(Hc, h);
+        });
       }
       // row sums of both key halves and the maxima for the output waves
 #pragma unroll
@@ -260,66 +282,62 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         }
       }
       lds_barrier();                                                        // E
-      lds_barrier();                                                        // F
     });
   } else {
     // ------------------------------------------------------- output waves --
     const int cw = wave - 4;                                  // columns cw*128 .. +128
+    const int g = lane >> 4, li = lane & 15;
+    const int vrow = 8 * g + (li >> 2);                       // value row (lo) of the transposed reads
+    const int vbase = vrow * 1024 + cw * 256 + (li & 1) * 8;
+    const int vkey = swz_v(vrow);                             // same for vrow + 32; vrow + 4 uses vkey ^ 8
+    const int vh = (li >> 1) & 1;
     for_each_chunk(p, [&](const Chunk& c) {
-      const int lane = threadIdx.x & 63;
       BlockWindow bw;
       bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
-      const int n = c.hi - c.lo;
-      PageShare<16> st;
-      value_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo), page_bytes), row_bytes, cw, lane);
-      value_share_store(st, kbuf0, cw, lane);
+      const int nh = half_pages(c);
+      // this wave's share of a half page: value rows 4w .. 4w+3
+      auto issue = [&](auto ic, int hh) {
+        const BufRsrc pg = dma_page(bw, c, hh, nh);
+        dma_value_rows4<kWideAux>(pg, hbuf(ic), hh & 1, 4 * wave, row_bytes, lane);
+      };
+      issue(I0{}, 0);
+      issue(I1{}, 1);
       f32x4 o[8][4];
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      lds_barrier();
-      for (int j = 0; j <= n; ++j) {
-        // Lane-dependent address parts are rebuilt every step from an opaque
-        // copy of the lane index: cheaper than pinning ~48 precomputed
-        // addresses in registers across the loop.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int gg = ln >> 4, ll = ln & 15;
-        const int vrow = 8 * gg + (ll >> 2);                 // value row (lo) of the transposed reads
-        const int vbase = vrow * 1024 + cw * 256 + (ll & 1) * 8;
-        const int vkey = swz_v(vrow);                        // same for vrow + 32; vrow + 4 uses vkey ^ 8
-        const int vh = (ll >> 1) & 1;
-        const bool more = j + 1 < n;
-        if (more) value_share_load<kWideAux>(st, page_of(p, bw.phys(c.lo + j + 1), page_bytes), row_bytes, cw, ln);
-        MLA_LDS char* prv = kbuf(j + 1);                     // page j-1
-        auto load_v = [&](int ks, int ct) {
+      dma_barrier<4>();
+
+      auto step = [&](auto Hc, int h) {
+        constexpr int H = decltype(Hc)::value;
+        MLA_LDS char* prv = hbuf(std::integral_constant<int, H + 3>{});   // half page h-1
+        issue(std::integral_constant<int, H + 2>{}, h + 2);
+        auto load_v = [&](int ct) {
           const int x = ((2 * ct + vh) ^ vkey) << 4;
-          const u32x2 lo4 = ld_lds_tr(prv + vbase + ks * 32768 + x);
-          const u32x2 hi4 = ld_lds_tr(prv + vbase + ks * 32768 + 4096 + (x ^ 128));
+          const u32x2 lo4 = ld_lds_tr(prv + vbase + x);
+          const u32x2 hi4 = ld_lds_tr(prv + vbase + 4096 + (x ^ 128));
           return u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
         };
-        // O^T[col][row] += V^T . P^T over keys ks*32 .. +32 of page j-1
-        auto pv_half = [&](int ks) {
-          u32x4 pf[4];
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            const int pr = rt * 16 + ll;
-            pf[rt] = ld_lds16(prv + kRopeOff + pr * 128 + (((ks * 4 + gg) ^ swz_r(pr)) << 4));
-          }
+        u32x4 pf[4];
+        // O^T[col][row] += V^T . P^T over the 32 keys of half page h-1, output
+        // column tiles ct0 .. ct0+3
+        auto pv = [&](int ct0) {
           u32x4 vf[2];
-          vf[0] = load_v(ks, 0);
+          vf[0] = load_v(ct0);
 #pragma unroll
-          for (int ct = 0; ct < 8; ++ct) {
-            if (ct + 1 < 8) vf[(ct + 1) & 1] = load_v(ks, ct + 1);
+          for (int i = 0; i < 4; ++i) {
+            if (i + 1 < 4) vf[(i + 1) & 1] = load_v(ct0 + i + 1);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) o[ct][rt] = Dt<T>::mfma32(vf[ct & 1], pf[rt], o[ct][rt]);
+            for (int rt = 0; rt < 4; ++rt) o[ct0 + i][rt] = Dt<T>::mfma32(vf[i & 1], pf[rt], o[ct0 + i][rt]);
           }
         };
-        if (j >= 1) {
+        if (h >= 1) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) pf[rt] = ld_lds16(prv + pchunk_off(rt * 16 + li, g));
           float a4[4];
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) a4[rt] = alpha_s[(j - 1) & 1][rt * 16 + ll];
+          for (int rt = 0; rt < 4; ++rt) a4[rt] = alpha_s[(h - 1) & 1][rt * 16 + li];
           const bool resc = (a4[0] != 1.f) | (a4[1] != 1.f) | (a4[2] != 1.f) | (a4[3] != 1.f);
           if (__any(resc)) {
 #pragma unroll
@@ -327,17 +345,20 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
 #pragma unroll
               for (int rt = 0; rt < 4; ++rt) o[ct][rt] *= a4[rt];
           }
-          pv_half(0);
+          pv(0);
         }
         lds_barrier();                                                      // A
-        if (j >= 1) pv_half(1);
-        lds_barrier();                                                      // C
-        if (more) value_share_store(st, kbuf(j + 1), cw, ln);
-        lds_barrier();                                                      // B
+        if (h >= 1) pv(4);
+        dma_barrier<4>();                                                   // B
+      };
+      for (int h0 = 0; h0 <= nh; h0 += 4) {
+        static_for<0, 4>([&](auto Hc) {
+          const int h = h0 + decltype(Hc)::value;
+          if (h <= nh) step(Hc, h);
+        });
       }
       lds_barrier();                                                        // E
       // epilogue: normalise, write the final output or an fp32 partial
-      const int g = lane >> 4, li = lane & 15;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int rl = rt * 16 + li;
@@ -359,7 +380,6 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           if (cw == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
         }
       }
-      lds_barrier();                                                        // F
     });
   }
 }
