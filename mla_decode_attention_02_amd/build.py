@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["mla_api.cpp", "mla_metadata.hip", "mla_splitkv.hip", "mla_combine.hip"]
+SOURCES = ["mla_api.cpp", "mla_metadata.hip", "mla_splitkv_wide.hip", "mla_splitkv_narrow.hip", "mla_combine.hip"]
 ARCH = "gfx950"
 
 
@@ -35,16 +35,18 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in the VGPR form: the online-softmax rescale works on
-    # them with plain VALU instructions, without AGPR round trips
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
 ]
+# Per-source extra flags.  The narrow kernel keeps its MFMA accumulators in the
+# VGPR form (its per-wave output rescale then needs no AGPR round trips); the
+# wide kernel runs faster with the default AGPR form (measured on MI355X).
+EXTRA_FLAGS = {"mla_splitkv_narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *COMMON_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), "-x", "hip", *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

@@ -195,7 +195,9 @@ mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream) {
   const mla::DecodeParams p = make_params(args);
   const int tile = tile_rows(p.rows);
   const int m_blocks = (p.rows + tile - 1) / tile;
-  hipError_t e = mla::launch_splitkv(p, args->dtype, m_blocks, tile == 16, static_cast<hipStream_t>(stream));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = tile == 16 ? mla::launch_splitkv_narrow(p, args->dtype, hs)
+                            : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
   if (e != hipSuccess) return hip_fail(e, "split-KV launch");
   return ok();
 }

@@ -8,8 +8,11 @@ namespace mla {
 
 struct DecodeParams;
 
-// Split-KV attention: grid (num_parts, m_blocks), 256 threads.  dtype 0 = bf16, 1 = fp16.
-hipError_t launch_splitkv(const DecodeParams& p, int dtype, int m_blocks, bool narrow, hipStream_t st);
+// Split-KV attention, 64-row tiles: grid (num_parts, m_blocks), 512 threads.
+// dtype 0 = bf16, 1 = fp16.
+hipError_t launch_splitkv_wide(const DecodeParams& p, int dtype, int m_blocks, hipStream_t st);
+// Split-KV attention, one tile of up to 16 rows: grid (num_parts), 256 threads.
+hipError_t launch_splitkv_narrow(const DecodeParams& p, int dtype, hipStream_t st);
 // Merge of split pieces: grid (batch, ceil(rows / 4)), 256 threads.
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st);
 // Tile schedule: one workgroup.

@@ -1,113 +1,8 @@
-// Split-KV MLA decode attention kernels for gfx950.
-//
-// What is computed (page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析",
-// sections "跷跷板调度的数学重构" and "辅助优化：可编程依赖启动与瓦片调度"): for one
-// request and one contiguous range of its 64-token pages, the softmax attention
-// of a tile of query rows over those keys, with an online (running-maximum)
-// softmax.  Scores and probabilities are kept in fp32 and exponentials use
-// exp2 with log2(e) folded into the scale (page "FlashMLA: 高性能GPU注意力机制计算库
-// 文件结构分析", section "4. Softmax数值稳定性优化").  A range that is a whole
-// request writes the final output and LSE; a piece of a split request writes an
-// fp32 partial output and its LSE for the combine kernel.
-//
-// Work decomposition.  One workgroup (4 waves, one per SIMD) per (scheduler
-// partition, tile of M query rows).  Pages stream HBM -> LDS with direct
-// 16-byte-per-lane loads into a double buffer (page "FlashMLA: ...文件结构分析",
-// sections "1. shared memory的双缓冲技术" and "5. 向量化与异步优化解析").
-// Scores are formed as S^T = K . Q^T on 16x16x32 MFMA so that each lane ends up
-// owning one query row; the output is accumulated as O^T = V^T . P^T, whose V^T
-// operand comes from transposed LDS reads of the same page (V = first 512
-// columns of K), so P and the rescale factors stay in the lane of their row.
-//   * narrow (s_q*h_q <= 16, M = 16): each wave takes 16 of a page's 64 keys and
-//     keeps its own running max, sum and 16x512 fp32 output; the four partial
-//     states are merged once at the end of the range.
-//   * wide (M = 64): each wave forms scores for 16 of the 64 rows over all 64
-//     keys, probabilities go through LDS, and each wave accumulates 128 of the
-//     512 output columns for all 64 rows (the fp32 output is split by columns
-//     across the waves, as the seesaw schedule splits it across warpgroups).
-#include "mla_common.hpp"
-#include "mla_internal.h"
+// Split-KV MLA decode attention, wide tile (64 query rows per workgroup).
+// Built with MFMA accumulators in AGPR form (the default).
+#include "mla_splitkv.hpp"
 
 namespace mla {
-
-template <typename T>
-__device__ __forceinline__ void load_q_frag(const DecodeParams& p, int b, int row, int g,
-                                            u32x4 (&qf)[18]) {
-  if (row < p.rows) {
-    const int tok = row / p.h_q;
-    const int head = row - tok * p.h_q;
-    const T* base = (const T*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = *(const u32x4*)(base + (ks * 4 + g) * 8);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = u32x4{0, 0, 0, 0};
-  }
-}
-
-// Store 4 consecutive output columns of one row (final output, dtype).
-template <typename T>
-__device__ __forceinline__ void store_out4(const DecodeParams& p, int b, int row, int col, f32x4 v) {
-  const int tok = row / p.h_q;
-  const int head = row - tok * p.h_q;
-  T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + col;
-  u32x2 w = {Dt<T>::pack2(v[0], v[1]), Dt<T>::pack2(v[2], v[3])};
-  *(u32x2*)dst = w;
-}
-
-__device__ __forceinline__ float lse_of(float m_log2, float l) {
-  return l > 0.f ? (m_log2 + __log2f(l)) * kLn2 : -INFINITY;
-}
-
-// One contiguous page range [lo, hi) of request b, as read from the schedule.
-struct Chunk {
-  int b, n, lo, hi, split, slot0, nsplit;
-};
-
-// Walk the pieces a scheduler partition owns, calling f(chunk) for each.
-template <typename F>
-__device__ __forceinline__ void for_each_chunk(const DecodeParams& p, F&& f) {
-  const int32_t* sc = p.sched + blockIdx.x * 8;
-  const int begin_req = ldu(sc + 0), begin_page = ldu(sc + 1);
-  const int end_req = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
-  for (int b = begin_req; b <= end_req; ++b) {
-    Chunk c;
-    c.b = b;
-    c.n = ldu(p.seqlens + b);
-    const int npages = (c.n + kPage - 1) / kPage;
-    c.lo = (b == begin_req) ? begin_page : 0;
-    c.hi = (b == end_req) ? end_page : npages;
-    if (c.lo >= c.hi) continue;
-    c.split = (b == begin_req) ? begin_split : 0;
-    c.slot0 = ldu(p.split_offsets + b);
-    c.nsplit = ldu(p.split_offsets + b + 1) - c.slot0;
-    f(c);
-  }
-}
-
-// Descriptor of physical page `phys` of the cache.
-__device__ __forceinline__ BufRsrc page_of(const DecodeParams& p, int phys, int page_bytes) {
-  return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0 * 2, page_bytes);
-}
-
-// Cache policy of page loads: the narrow kernel reads every page once; in the
-// wide kernel the row tiles of one request read the same pages and may meet in L2.
-constexpr int kNarrowAux = 2;
-constexpr int kWideAux = 0;
-
-// Page loop driver: pages [lo, hi) alternate between two LDS buffers.  The loop
-// is unrolled by two so that the buffer roles and the register stage a step
-// uses are compile-time: step(parity, cur, nxt, pg) processes page pg from
-// `cur` while the next page is written into `nxt`.
-template <typename Step>
-__device__ __forceinline__ void page_loop(int lo, int hi, MLA_LDS char* buf0, MLA_LDS char* buf1,
-                                          Step&& step) {
-  for (int pg = lo; pg < hi; pg += 2) {
-    step(std::integral_constant<int, 0>{}, buf0, buf1, pg);
-    if (pg + 1 >= hi) break;
-    step(std::integral_constant<int, 1>{}, buf1, buf0, pg + 1);
-  }
-}
 
 // ------------------------------------------------------------------ wide --
 // 64 query rows per workgroup, 8 waves (two per SIMD) in two roles, so that on
@@ -384,171 +279,10 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   }
 }
 
-// ---------------------------------------------------------------- narrow --
-template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char kbuf0_raw[kPageBytes];
-  __shared__ __attribute__((aligned(1024))) char kbuf1_raw[kPageBytes];
-  __shared__ float m_w[kWaves][16];
-  __shared__ float l_w[kWaves][16];
-  MLA_LDS char* kbuf0 = (MLA_LDS char*)kbuf0_raw;
-  MLA_LDS char* kbuf1 = (MLA_LDS char*)kbuf1_raw;
-  constexpr int kMergeStride = kDV + 4;   // floats per row of the merge buffer
-  static_assert(2 * 16 * kMergeStride * 4 <= kPageBytes, "merge buffer fits two waves per page buffer");
-
-  const int tid = threadIdx.x;
-  const int wave = wave_id(), lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int row_bytes = (int)(p.k_s1 * 2);
-  const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
-
-  for_each_chunk(p, [&](const Chunk& c) {
-    BlockWindow bw;
-    bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
-    u32x4 qf[18];
-    load_q_frag<T>(p, c.b, li, g, qf);
-    const int cnt = li < p.rows ? visible_count(c.n, p.s_q, li / p.h_q, p.causal) : 0;
-    float m_run = -INFINITY, l_part = 0.f;
-    f32x4 o[32];
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int krow = wave * 16 + li;                       // key row of the score operand
-    const int vrow = wave * 16 + 4 * g + (li >> 2);        // value row of the transposed reads
-    const int vbase = vrow * 1024 + (li & 1) * 8;
-    const int vkey = swz_v(vrow);
-    const int vh = (li >> 1) & 1;
-
-    // two pages in flight in registers while a third is read from LDS
-    PageStage st[2];
-    stage_load<kNarrowAux>(st[0], page_of(p, bw.phys(c.lo), page_bytes), row_bytes, wave, lane);
-    if (c.lo + 1 < c.hi) stage_load<kNarrowAux>(st[1], page_of(p, bw.phys(c.lo + 1), page_bytes), row_bytes, wave, lane);
-    stage_store(st[0], kbuf0, wave, lane);
-    lds_barrier();
-    page_loop(c.lo, c.hi, kbuf0, kbuf1, [&](auto par, MLA_LDS char* cur, MLA_LDS char* nxt, int pg) {
-      constexpr int P = decltype(par)::value;   // st[P] held page pg, st[P ^ 1] holds pg + 1
-      if (pg + 2 < c.hi) stage_load<kNarrowAux>(st[P], page_of(p, bw.phys(pg + 2), page_bytes), row_bytes, wave, lane);
-
-      // S^T for keys wave*16 .. +16 of the page, all 16 rows; operand reads
-      // run two steps ahead of the MFMAs
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      u32x4 kf[3];
-      kf[0] = ld_lds16(cur + kchunk_off<0>(krow, g));
-      kf[1] = ld_lds16(cur + kchunk_off<1>(krow, g));
-      static_for<0, 18>([&](auto ksc) {
-        constexpr int ks = decltype(ksc)::value;
-        if constexpr (ks + 2 < 18) kf[(ks + 2) % 3] = ld_lds16(cur + kchunk_off<ks + 2>(krow, g));
-        s = Dt<T>::mfma32(kf[ks % 3], qf[ks], s);
-      });
-      const int key0 = pg * kPage + wave * 16 + 4 * g;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float t = (key0 + r < cnt) ? s[r] * p.scale_log2 : -INFINITY;
-        s[r] = t;
-        mx = fmaxf(mx, t);
-      }
-      mx = max_across_groups(mx);
-      float alpha = 1.f;
-      if (mx > m_run + kRescaleSlack) {
-        alpha = exp2f(m_run - mx);
-        m_run = mx;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(s[r] - msub);
-        rs += s[r];
-      }
-      l_part = l_part * alpha + rs;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
-      }
-      const u32x2 pk = {Dt<T>::pack2(s[0], s[1]), Dt<T>::pack2(s[2], s[3])};
-      constexpr int kAhead = 4;
-      u32x2 vf[kAhead + 1];
-      auto vaddr = [&](int ct) { return cur + vbase + (ct >> 3) * 256 + ((((2 * ct) & 15) + vh) ^ vkey) * 16; };
-#pragma unroll
-      for (int ct = 0; ct < kAhead; ++ct) vf[ct] = ld_lds_tr(vaddr(ct));
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) {
-        if (ct + kAhead < 32) vf[(ct + kAhead) % (kAhead + 1)] = ld_lds_tr(vaddr(ct + kAhead));
-        o[ct] = Dt<T>::mfma16(vf[ct % (kAhead + 1)], pk, o[ct]);
-      }
-      if (pg + 1 < c.hi) stage_store(st[P ^ 1], nxt, wave, lane);
-      lds_barrier();
-    });
-
-    // merge the four per-wave states of this range
-    const float lw = sum_across_groups(l_part);
-    if (g == 0) {
-      m_w[wave][li] = m_run;
-      l_w[wave][li] = lw;
-    }
-    lds_barrier();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_w[w][li]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      L += (m_w[w][li] == -INFINITY) ? 0.f : l_w[w][li] * exp2f(m_w[w][li] - M);
-    const float f = (L > 0.f && m_run != -INFINITY) ? exp2f(m_run - M) / L : 0.f;
-    // merge buffer: [wave][16 rows][kMergeStride] floats, waves 0-1 in the first
-    // page buffer and waves 2-3 in the second
-    auto mrow = [&](int w, int row) -> float* {
-      return (float*)(w < 2 ? kbuf0_raw : kbuf1_raw) + ((w & 1) * 16 + row) * kMergeStride;
-    };
-    {
-      float* dst = mrow(wave, li);
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) *(f32x4*)(dst + ct * 16 + 4 * g) = o[ct] * f;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int idx = tid + kThreads * k;
-      const int row = idx >> 7;
-      const int col = (idx & 127) * 4;
-      if (row < p.rows) {
-        f32x4 acc = *(f32x4*)(mrow(0, row) + col);
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) acc += *(f32x4*)(mrow(w, row) + col);
-        if (c.nsplit == 1) {
-          store_out4<T>(p, c.b, row, col, acc);
-        } else {
-          const int64_t slot = c.slot0 + c.split;
-          *(f32x4*)(p.part_o + (slot * p.rows + row) * kDV + col) = acc;
-        }
-      }
-    }
-    if (tid < 16 && tid < p.rows) {
-      float Mx = -INFINITY, Ls = 0.f;
-      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, m_w[w][tid]);
-      for (int w = 0; w < kWaves; ++w)
-        Ls += (m_w[w][tid] == -INFINITY) ? 0.f : l_w[w][tid] * exp2f(m_w[w][tid] - Mx);
-      const float lse = lse_of(Mx, Ls);
-      if (c.nsplit == 1) p.lse[(int64_t)c.b * p.rows + tid] = lse;
-      else p.part_lse[(int64_t)(c.slot0 + c.split) * p.rows + tid] = lse;
-    }
-    lds_barrier();
-  });
-}
-
-template <typename T>
-static hipError_t launch_splitkv_t(const DecodeParams& p, int m_blocks, bool narrow, hipStream_t st) {
-  if (narrow) {
-    hipLaunchKernelGGL(splitkv_narrow_kernel<T>, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
-  } else {
-    hipLaunchKernelGGL(splitkv_wide_kernel<T>, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
-  }
+hipError_t launch_splitkv_wide(const DecodeParams& p, int dtype, int m_blocks, hipStream_t st) {
+  if (dtype == 0) hipLaunchKernelGGL(splitkv_wide_kernel<__bf16>, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
+  else hipLaunchKernelGGL(splitkv_wide_kernel<_Float16>, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
   return hipGetLastError();
-}
-
-hipError_t launch_splitkv(const DecodeParams& p, int dtype, int m_blocks, bool narrow, hipStream_t st) {
-  return dtype == 0 ? launch_splitkv_t<__bf16>(p, m_blocks, narrow, st)
-                    : launch_splitkv_t<_Float16>(p, m_blocks, narrow, st);
 }
 
 }  // namespace mla
