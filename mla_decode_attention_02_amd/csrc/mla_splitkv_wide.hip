@@ -8,35 +8,31 @@ namespace mla {
 // 64 query rows per workgroup, 8 waves (two per SIMD) in two roles, so that on
 // every SIMD the MFMAs of one role overlap the softmax arithmetic and LDS
 // traffic of the other (the MI355X counterpart of the seesaw schedule's two
-// alternating warpgroups).  Keys are processed in half pages of 32.
+// alternating warpgroups).  Keys are processed in half pages of 32; step t
+// scores half page t and accumulates half page t-1.
 //   * score waves 0..3, (rg, kg) = (w >> 1, w & 1): raw scores S^T for query
 //     rows rg*32 .. +32 (two 16-row tiles, Q fragments in registers) and keys
 //     kg*16 .. +16 of half page t; each K fragment read from LDS feeds two
-//     MFMAs.  The scores go to an fp32 tile in LDS.  These waves also issue
-//     all the HBM -> LDS loads, spread over their MFMA stream.
-//   * output waves 4..7: wave c owns the softmax of rows 16c .. 16c+15 (all 32
-//     keys of the half page, so no cross-wave maximum exchange), writes their
-//     probabilities P(t) and rescale factors to LDS, and accumulates
-//     O^T += V^T . P^T for output columns 128c .. +128 of all 64 rows.
-// Step t has two workgroup barriers: X(t) after the scores S(t) are written,
-// Y(t) after P(t) is written.  Between Y(t-1) and X(t) the output waves form
-// P(t-1).V(t-1) while the score waves finish S(t); between X(t) and Y(t) the
-// output waves run the softmax of t while the score waves start S(t+1).
+//     MFMAs.  The scores go to one of two fp32 tiles in LDS.  These waves also
+//     issue all the HBM -> LDS loads, spread over their MFMA stream.
+//   * output waves 4..7, (rh, ch) = (c >> 1, c & 1): O^T for rows rh*32 .. +32
+//     and columns ch*256 .. +256 (128 fp32 registers per lane).  Each runs the
+//     online softmax of its 32 rows itself (the two waves of a row half do the
+//     same arithmetic), so the probabilities go straight from its registers
+//     into the MFMA operand and no wave waits for another's P.
+// One workgroup barrier per step (scores of t written, loads of t+1 landed).
 // Half pages stream HBM -> LDS by direct (LDS-DMA) loads into four buffers
 // named at compile time (the step loop is unrolled by four, so the compiler
 // can tell the LDS reads of one buffer from the loads in flight into
-// another); the loads of half page t+2 are issued during step t and waited
-// for at X(t+1).
+// another); the loads of half page t+2 are issued during step t.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char hb0_raw[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) char hb1_raw[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) char hb2_raw[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) char hb3_raw[kHalfBytes];
-  __shared__ __attribute__((aligned(1024))) char s_raw[64 * 32 * 4];   // S(t), fp32 [row][32 keys]
-  __shared__ float alpha_s[64];
-  __shared__ float l_s[64];
-  __shared__ float m_s[64];
+  __shared__ __attribute__((aligned(1024))) char s_raw[2][64 * 32 * 4];   // S(t), fp32 [row][32 keys]
+  static_assert(4 * kHalfBytes + 2 * 64 * 32 * 4 <= 163840, "LDS budget of one workgroup");
   auto hbuf = [&](auto ic) -> MLA_LDS char* {
     constexpr int i = decltype(ic)::value & 3;
     if constexpr (i == 0) return (MLA_LDS char*)hb0_raw;
@@ -44,8 +40,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
     else if constexpr (i == 2) return (MLA_LDS char*)hb2_raw;
     else return (MLA_LDS char*)hb3_raw;
   };
-  MLA_LDS char* const stile = (MLA_LDS char*)s_raw;
-  // 16-byte chunk c (keys 4c .. 4c+3) of row `row` of the score tile
+  auto stile = [&](auto ic) -> MLA_LDS char* {
+    constexpr int i = decltype(ic)::value & 1;
+    return (MLA_LDS char*)s_raw[i];
+  };
+  // 16-byte chunk c (keys 4c .. 4c+3) of row `row` of a score tile
   auto schunk = [](int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); };
 
   const int wave = wave_id();
@@ -87,11 +86,13 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
       auto piece = [&](auto ic, int hh, BufRsrc pg, int i) {
         MLA_LDS char* hb = hbuf(ic);
         const int half = hh & 1;
+        int ln = lane;                 // opaque: offsets are rebuilt, not kept live
+        asm volatile("" : "+v"(ln));
         if (i < 8) {
           const int r = 8 * wave + i;
-          dma16<kWideAux>(pg, hb + r * 1024, (lane ^ swz_v(r)) << 4, (half * kHalfRows + r) * row_bytes);
+          dma16<kWideAux>(pg, hb + r * 1024, (ln ^ swz_v(r)) << 4, (half * kHalfRows + r) * row_bytes);
         } else {
-          dma_rope_rows8<kWideAux>(pg, hb, half, wave, row_bytes, lane);
+          dma_rope_rows8<kWideAux>(pg, hb, half, wave, row_bytes, ln);
         }
       };
       {
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
       }
       dma_barrier<9>();                                                     // X(-1)
 
+      // step t < nh: S(t) into score tile t&1; loads of half page t+2
       auto step = [&](auto Hc, int t) {
         constexpr int H = decltype(Hc)::value;
         MLA_LDS char* cur = hbuf(Hc);
@@ -119,18 +121,13 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           constexpr int ks = decltype(ksc)::value;
           if constexpr (ks + kAhead < 18) kf[(ks + kAhead) % (kAhead + 1)] = ld_lds16(cur + hchunk_off<ks + kAhead>(krow, g));
           if constexpr (ks % 2 == 0) piece(std::integral_constant<int, H + 2>{}, t + 2, pg, ks / 2);
-          if constexpr (ks == 10) {
-            // Y(t-1): the output waves have published P(t-1); nothing of this
-            // wave depends on it, so no wait for outstanding LDS reads
-            if (t >= 1) asm volatile("s_barrier" ::: "memory");
-          }
           s0 = Dt<T>::mfma32(kf[ks % (kAhead + 1)], qf[0][ks], s0);
           s1 = Dt<T>::mfma32(kf[ks % (kAhead + 1)], qf[1][ks], s1);
         });
-        // raw scores to the tile (the softmax of t-1 has read the previous ones)
+        MLA_LDS char* st = stile(Hc);
         const int row0 = rg * 32 + li;
-        *(MLA_LDS f32x4*)(stile + schunk(row0, kg * 4 + g)) = s0;
-        *(MLA_LDS f32x4*)(stile + schunk(row0 + 16, kg * 4 + g)) = s1;
+        *(MLA_LDS f32x4*)(st + schunk(row0, kg * 4 + g)) = s0;
+        *(MLA_LDS f32x4*)(st + schunk(row0 + 16, kg * 4 + g)) = s1;
         dma_barrier<9>();                                                   // X(t)
       };
       // whole groups of four steps, then the tail: every step of the loop body
@@ -141,37 +138,42 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         const int t = t0 + decltype(Hc)::value;
         if (t < nh) step(Hc, t);
       });
-      asm volatile("s_barrier" ::: "memory");                               // Y(nh-1)
-      lds_barrier();                                                        // E
+      lds_barrier();                                                        // X(nh)
     });
   } else {
     // ------------------------------------------------------- output waves --
-    const int cw = wave - 4;                                  // columns cw*128 .. +128
-    const int srow = cw * 16 + li;                            // softmax row of this lane
+    const int cw = wave - 4;
+    const int rh = cw >> 1, ch = cw & 1;      // rows rh*32 .. +32, columns ch*256 .. +256
     for_each_chunk(p, [&](const Chunk& c) {
       const int nh = half_pages(c);
-      const int qrow = mrow0 + srow;
-      const int cnt = qrow < p.rows ? visible_count(c.n, p.s_q, qrow / p.h_q, p.causal) : 0;
-      float m_run = -INFINITY;   // running max of row srow, log2 units
-      float l_part = 0.f;        // this lane's share of its running sum
-      f32x4 o[8][4];
+      int cnt[2];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+      for (int rt = 0; rt < 2; ++rt) {
+        const int qrow = mrow0 + rh * 32 + rt * 16 + li;
+        cnt[rt] = qrow < p.rows ? visible_count(c.n, p.s_q, qrow / p.h_q, p.causal) : 0;
+      }
+      float m_run[2] = {-INFINITY, -INFINITY};   // running max per row, log2 units
+      float l_part[2] = {0.f, 0.f};              // this lane's share of the running sums
+      f32x4 o[16][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
       lds_barrier();                                                        // X(-1)
 
-      // O *= alpha(t-1); O^T[col][row] += V^T . P^T over half page t-1
-      auto pv = [&](auto Pc) {
-        MLA_LDS char* prv = hbuf(Pc);
+      // step t >= 1: softmax of half page t-1 for this wave's 32 rows, then
+      // O^T += V^T . P^T over it
+      auto step = [&](auto Hc, int t) {
+        constexpr int H = decltype(Hc)::value;
+        MLA_LDS char* st = stile(std::integral_constant<int, H + 1>{});   // S(t-1)
+        MLA_LDS char* prv = hbuf(std::integral_constant<int, H + 3>{});   // half page t-1
         // Lane-dependent read addresses are rebuilt here from an opaque copy of
-        // the lane index: cheaper than keeping ~64 of them (16 per buffer)
-        // alive in registers across the step loop.
+        // the lane index: cheaper than keeping them alive across the loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int lg = ln >> 4, ll = ln & 15;
         const int vrow = 8 * lg + (ll >> 2);                  // value row (lo) of the transposed reads
-        const int vbase = vrow * 1024 + cw * 256 + (ll & 1) * 8;
+        const int vbase = vrow * 1024 + ch * 512 + (ll & 1) * 8;
         const int vkey = swz_v(vrow);                         // vrow + 4 uses vkey ^ 8
         const int vh = (ll >> 1) & 1;
         auto load_v = [&](int ct) {
@@ -180,99 +182,94 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           const u32x2 hi4 = ld_lds_tr(prv + vbase + 4096 + (x ^ 128));
           return u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
         };
-        // every operand read of the step is issued before the first MFMA
-        float a4[4];
+        // scores of rows rh*32 + rt*16 + ll, keys 8lg .. 8lg+7
+        f32x4 sv[2][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) a4[rt] = alpha_s[rt * 16 + ll];
-        u32x4 pf[4];
+        for (int rt = 0; rt < 2; ++rt) {
+          const int row = rh * 32 + rt * 16 + ll;
+          sv[rt][0] = *(MLA_LDS f32x4*)(st + schunk(row, 2 * lg));
+          sv[rt][1] = *(MLA_LDS f32x4*)(st + schunk(row, 2 * lg + 1));
+        }
+        constexpr int kVAhead = 4;
+        u32x4 vf[kVAhead + 1];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) pf[rt] = ld_lds16(prv + pchunk_off(rt * 16 + ll, lg));
-        u32x4 vf[8];
+        for (int ct = 0; ct < kVAhead; ++ct) vf[ct] = load_v(ct);
+        // online softmax; the lane's 8 probabilities per row tile are the
+        // P^T operand of that tile as they stand
+        const int key0 = (2 * c.lo + t - 1) * kHalfRows + 8 * lg;
+        u32x4 pf[2];
+        float alpha[2];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) vf[ct] = load_v(ct);
-        const bool resc = (a4[0] != 1.f) | (a4[1] != 1.f) | (a4[2] != 1.f) | (a4[3] != 1.f);
-        if (__any(resc)) {
+        for (int rt = 0; rt < 2; ++rt) {
+          float x[8] = {sv[rt][0][0], sv[rt][0][1], sv[rt][0][2], sv[rt][0][3],
+                        sv[rt][1][0], sv[rt][1][1], sv[rt][1][2], sv[rt][1][3]};
+          float mx = -INFINITY;
 #pragma unroll
-          for (int ct = 0; ct < 8; ++ct)
+          for (int j = 0; j < 8; ++j) {
+            x[j] = (key0 + j < cnt[rt]) ? x[j] * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[j]);
+          }
+          mx = max_across_groups(mx);
+          alpha[rt] = 1.f;
+          if (mx > m_run[rt] + kRescaleSlack) {
+            alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - mx);
+            m_run[rt] = mx;
+          }
+          const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
+          float rs = 0.f;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) o[ct][rt] *= a4[rt];
+          for (int j = 0; j < 8; ++j) {
+            x[j] = __builtin_amdgcn_exp2f(x[j] - msub);
+            rs += x[j];
+          }
+          l_part[rt] = l_part[rt] * alpha[rt] + rs;
+          pf[rt] = u32x4{Dt<T>::pack2(x[0], x[1]), Dt<T>::pack2(x[2], x[3]), Dt<T>::pack2(x[4], x[5]),
+                         Dt<T>::pack2(x[6], x[7])};
+        }
+        // alpha is per row = per lane column of the accumulator tiles
+        if (__any((alpha[0] != 1.f) | (alpha[1] != 1.f))) {
+#pragma unroll
+          for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) o[ct][rt] *= alpha[rt];
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 16; ++ct) {
+          if (ct + kVAhead < 16) vf[(ct + kVAhead) % (kVAhead + 1)] = load_v(ct + kVAhead);
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) o[ct][rt] = Dt<T>::mfma32(vf[ct], pf[rt], o[ct][rt]);
+          for (int rt = 0; rt < 2; ++rt) o[ct][rt] = Dt<T>::mfma32(vf[ct % (kVAhead + 1)], pf[rt], o[ct][rt]);
+        }
       };
-      // step t accumulates half page t-1 and, for t < nh, runs the softmax of t
-      auto step = [&](auto Hc, int t) {
-        constexpr int H = decltype(Hc)::value;
-        if (t >= 1) pv(std::integral_constant<int, H + 3>{});
-        if (t == nh) return;
+      // step t in 0 .. nh; every step ends with X(t)
+      auto stepx = [&](auto Hc, int t) {
+        if (t >= 1) step(Hc, t);
         lds_barrier();                                                      // X(t)
-        // softmax of row srow over keys 8g .. 8g+7 of half page t
-        const f32x4 sa = *(MLA_LDS f32x4*)(stile + schunk(srow, 2 * g));
-        const f32x4 sb = *(MLA_LDS f32x4*)(stile + schunk(srow, 2 * g + 1));
-        float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-        const int key0 = (2 * c.lo + t) * kHalfRows + 8 * g;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x[j] = (key0 + j < cnt) ? x[j] * p.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, x[j]);
-        }
-        mx = max_across_groups(mx);
-        float alpha = 1.f;
-        if (mx > m_run + kRescaleSlack) {
-          alpha = __builtin_amdgcn_exp2f(m_run - mx);
-          m_run = mx;
-        }
-        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-        float rs = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x[j] = __builtin_amdgcn_exp2f(x[j] - msub);
-          rs += x[j];
-        }
-        l_part = l_part * alpha + rs;
-        const u32x4 pk = {Dt<T>::pack2(x[0], x[1]), Dt<T>::pack2(x[2], x[3]), Dt<T>::pack2(x[4], x[5]),
-                          Dt<T>::pack2(x[6], x[7])};
-        *(MLA_LDS u32x4*)(hbuf(Hc) + pchunk_off(srow, g)) = pk;
-        if (g == 0) alpha_s[srow] = alpha;
-        lds_barrier();                                                      // Y(t)
       };
       int t0 = 0;
-      for (; t0 + 4 <= nh + 1; t0 += 4) static_for<0, 4>([&](auto Hc) { step(Hc, t0 + decltype(Hc)::value); });
+      for (; t0 + 4 <= nh + 1; t0 += 4) static_for<0, 4>([&](auto Hc) { stepx(Hc, t0 + decltype(Hc)::value); });
       static_for<0, 3>([&](auto Hc) {
         const int t = t0 + decltype(Hc)::value;
-        if (t <= nh) step(Hc, t);
+        if (t <= nh) stepx(Hc, t);
       });
-      {
-        const float lw = sum_across_groups(l_part);
-        if (g == 0) {
-          l_s[srow] = lw;
-          m_s[srow] = m_run;
-        }
-      }
-      lds_barrier();                                                        // E
       // epilogue: normalise, write the final output or an fp32 partial
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int rl = rt * 16 + li;
-        const int row = mrow0 + rl;
+      for (int rt = 0; rt < 2; ++rt) {
+        const float l = sum_across_groups(l_part[rt]);
+        const int row = mrow0 + rh * 32 + rt * 16 + li;
         if (row >= p.rows) continue;
-        const float l = l_s[rl];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        const float lse = lse_of(m_s[rl], l);
+        const float lse = lse_of(m_run[rt], l);
         if (c.nsplit == 1) {
 #pragma unroll
-          for (int ct = 0; ct < 8; ++ct)
-            store_out4<T>(p, c.b, row, cw * 128 + ct * 16 + 4 * g, o[ct][rt] * inv);
-          if (cw == 0 && g == 0) p.lse[(int64_t)c.b * p.rows + row] = lse;
+          for (int ct = 0; ct < 16; ++ct)
+            store_out4<T>(p, c.b, row, ch * 256 + ct * 16 + 4 * g, o[ct][rt] * inv);
+          if (ch == 0 && g == 0) p.lse[(int64_t)c.b * p.rows + row] = lse;
         } else {
           const int64_t slot = c.slot0 + c.split;
-          float* dst = p.part_o + (slot * p.rows + row) * kDV + cw * 128 + 4 * g;
+          float* dst = p.part_o + (slot * p.rows + row) * kDV + ch * 256 + 4 * g;
 #pragma unroll
-          for (int ct = 0; ct < 8; ++ct) *(f32x4*)(dst + ct * 16) = o[ct][rt] * inv;
-          if (cw == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+          for (int ct = 0; ct < 16; ++ct) *(f32x4*)(dst + ct * 16) = o[ct][rt] * inv;
+          if (ch == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
         }
       }
     });
