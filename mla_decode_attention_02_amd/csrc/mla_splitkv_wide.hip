@@ -190,26 +190,30 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           sv[rt][0] = *(MLA_LDS f32x4*)(st + schunk(row, 2 * lg));
           sv[rt][1] = *(MLA_LDS f32x4*)(st + schunk(row, 2 * lg + 1));
         }
-        constexpr int kVAhead = 4;
+        constexpr int kVAhead = 6;
         u32x4 vf[kVAhead + 1];
 #pragma unroll
         for (int ct = 0; ct < kVAhead; ++ct) vf[ct] = load_v(ct);
         // online softmax; the lane's 8 probabilities per row tile are the
         // P^T operand of that tile as they stand
         const int key0 = (2 * c.lo + t - 1) * kHalfRows + 8 * lg;
+        // whole half page visible to both row tiles of this lane: no masking
+        const bool full = key0 + 8 <= min(cnt[0], cnt[1]);
         u32x4 pf[2];
         float alpha[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           float x[8] = {sv[rt][0][0], sv[rt][0][1], sv[rt][0][2], sv[rt][0][3],
                         sv[rt][1][0], sv[rt][1][1], sv[rt][1][2], sv[rt][1][3]};
-          float mx = -INFINITY;
+          if (!full) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            x[j] = (key0 + j < cnt[rt]) ? x[j] * p.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, x[j]);
+            for (int j = 0; j < 8; ++j) x[j] = (key0 + j < cnt[rt]) ? x[j] : -INFINITY;
           }
-          mx = max_across_groups(mx);
+          float mx = x[0];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+          // scores are raw dot products: scale_log2 > 0 commutes with the max
+          mx = max_across_groups(mx) * p.scale_log2;
           alpha[rt] = 1.f;
           if (mx > m_run[rt] + kRescaleSlack) {
             alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - mx);
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           float rs = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            x[j] = __builtin_amdgcn_exp2f(x[j] - msub);
+            x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], p.scale_log2, -msub));
             rs += x[j];
           }
           l_part[rt] = l_part[rt] * alpha[rt] + rs;
