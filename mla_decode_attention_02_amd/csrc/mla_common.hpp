@@ -296,9 +296,10 @@ __device__ __forceinline__ void dma_rope_rows8(BufRsrc page, MLA_LDS char* hb, i
 // own wait placement knows which loads are still in flight after it.
 template <int N>
 __device__ __forceinline__ void dma_barrier() {
-  static_assert(N >= 0 && N <= 15, "vmcnt immediate");
-  // s_waitcnt fields: vmcnt [3:0], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15 = no wait)
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N <= 63, "vmcnt immediate");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] (7 = no wait),
+  // lgkmcnt [11:8] (15 = no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 

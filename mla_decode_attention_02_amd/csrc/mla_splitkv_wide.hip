@@ -30,7 +30,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char hb1_raw[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) char hb2_raw[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) char hb3_raw[kHalfBytes];
-  __shared__ __attribute__((aligned(1024))) char pb_raw[2][4096];   // P(t), key-group major
+  __shared__ __attribute__((aligned(1024))) char pb_raw[2][4096];   // P(t), key-slot-group major
   __shared__ float alpha_s[2][64];
   __shared__ float l_s[64];
   __shared__ float m_s[64];
@@ -45,7 +45,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
     constexpr int i = decltype(ic)::value & 1;
     return (MLA_LDS char*)pb_raw[i];
   };
-  // byte offset of the 16 bytes of keys 8c .. 8c+7 of row `row` in a P tile
+  // The contraction of P.V over the 32 keys of a half page runs in a permuted
+  // key order: k-slots 8c .. 8c+7 hold keys 4c .. 4c+3 and 16+4c .. 16+4c+3, the
+  // eight scores one lane of a score wave owns (key c of the two 16-key score
+  // tiles), so that lane writes its probabilities with a single 16-byte store.
+  // Byte offset of the 16 bytes of slot group c of row `row` in a P tile:
   auto poff = [](int row, int c) { return c * 1024 + row * 16; };
 
   const int wave = wave_id();
@@ -157,11 +161,12 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           rs += x[j];
         }
         l_part = l_part * alpha + rs;
+        // one store: two stores to this tile would be merged into a single
+        // instruction that waits for every load in flight
         MLA_LDS char* pb = pbuf(Hc);
-        const u32x2 p0 = {Dt<T>::pack2(x[0], x[1]), Dt<T>::pack2(x[2], x[3])};
-        const u32x2 p1 = {Dt<T>::pack2(x[4], x[5]), Dt<T>::pack2(x[6], x[7])};
-        *(MLA_LDS u32x2*)(pb + poff(srow, g >> 1) + (g & 1) * 8) = p0;
-        *(MLA_LDS u32x2*)(pb + poff(srow, 2 + (g >> 1)) + (g & 1) * 8) = p1;
+        *(MLA_LDS u32x4*)(pb + poff(srow, g)) =
+            u32x4{Dt<T>::pack2(x[0], x[1]), Dt<T>::pack2(x[2], x[3]), Dt<T>::pack2(x[4], x[5]),
+                  Dt<T>::pack2(x[6], x[7])};
         if (g == 0) alpha_s[H & 1][srow] = alpha;
         dma_barrier<9>();                                                   // X(t)
       };
@@ -204,14 +209,15 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int lg = ln >> 4, ll = ln & 15;
-        const int vrow = 8 * lg + (ll >> 2);                  // value row (lo) of the transposed reads
+        // slots 8lg .. 8lg+7 = keys 4lg .. 4lg+3 (lo) and 16+4lg .. 16+4lg+3 (hi)
+        const int vrow = 4 * lg + (ll >> 2);                  // value row (lo) of the transposed reads
         const int vbase = vrow * 1024 + cw * 256 + (ll & 1) * 8;
-        const int vkey = swz_v(vrow);                         // vrow + 4 uses vkey ^ 8
+        const int vkey = swz_v(vrow);                         // the same for vrow + 16
         const int vh = (ll >> 1) & 1;
         auto load_v = [&](int ct) {
           const int x = ((2 * ct + vh) ^ vkey) << 4;
           const u32x2 lo4 = ld_lds_tr(prv + vbase + x);
-          const u32x2 hi4 = ld_lds_tr(prv + vbase + 4096 + (x ^ 128));
+          const u32x2 hi4 = ld_lds_tr(prv + vbase + 16 * 1024 + x);
           return u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
         };
         float a4[4];
