@@ -3,53 +3,101 @@
 // combine kernel that follows splitkv_mla).  For a request cut into pieces k
 // with normalised partial outputs O_k and LSE_k:
 //   LSE = log sum_k exp(LSE_k),   O = sum_k exp(LSE_k - LSE) * O_k.
-// One wave per query row; each lane owns 8 of the 512 columns.  Requests with
-// no cached token get O = 0 and LSE = -inf; whole (unsplit) requests were
-// already written by the split-KV kernel and are skipped.
+// One wave per (query row, half of the 512 columns); each lane owns 4 columns.
+// The lanes load the pieces' LSEs together (lane k holds piece k of a group of
+// 64) and reduce them across the wave, while the first eight pieces' data loads
+// are already in flight; the weighted sum keeps eight pieces' loads in flight
+// per lane, so a request cut into many pieces is not a chain of dependent
+// memory round trips.  Requests with no cached token get
+// O = 0 and LSE = -inf; whole (unsplit) requests were already written by the
+// split-KV kernel and are skipped.
 #include "mla_common.hpp"
 #include "mla_internal.h"
 
 namespace mla {
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
+  return x;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + wave;
+  const int col = blockIdx.z * 256 + lane * 4;
   if (row >= p.rows) return;
-  const int s0 = p.split_offsets[b];
-  const int ns = p.split_offsets[b + 1] - s0;
+  const int s0 = ldu(p.split_offsets + b);
+  const int ns = ldu(p.split_offsets + b + 1) - s0;
   if (ns == 1) return;
-  const int tok = row / p.h_q;
-  const int head = row - tok * p.h_q;
-  T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + lane * 8;
-  float* lse_dst = p.lse + (int64_t)b * p.rows + row;
+  const float* lse_k = p.part_lse + (int64_t)s0 * p.rows + row;   // stride p.rows per piece
 
-  float mx = -INFINITY;
-  for (int k = 0; k < ns; ++k) mx = fmaxf(mx, p.part_lse[(int64_t)(s0 + k) * p.rows + row]);
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const float* src = p.part_o + ((int64_t)s0 * p.rows + row) * kDV + col;
+  const int64_t piece = (int64_t)p.rows * kDV;                      // floats between pieces
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = -INFINITY;
-  if (mx != -INFINITY) {
-    float sum = 0.f;
-    for (int k = 0; k < ns; ++k)
-      sum += __builtin_amdgcn_exp2f((p.part_lse[(int64_t)(s0 + k) * p.rows + row] - mx) * kLog2e);
-    L = mx + __logf(sum);
-    for (int k = 0; k < ns; ++k) {
-      const int64_t slot = s0 + k;
-      const float w = __builtin_amdgcn_exp2f((p.part_lse[slot * p.rows + row] - L) * kLog2e);
-      const float* src = p.part_o + (slot * p.rows + row) * kDV + lane * 8;
-      acc0 += w * *(const f32x4*)src;
-      acc1 += w * *(const f32x4*)(src + 4);
+  if (ns <= 64) {
+    // the first eight pieces' data loads go out together with the LSE loads
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = u < ns ? *(const f32x4*)(src + u * piece) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float lk = lane < ns ? lse_k[(int64_t)lane * p.rows] : -INFINITY;
+    const float mx = wave_max(lk);
+    if (mx != -INFINITY) {
+      const float e = lane < ns ? __builtin_amdgcn_exp2f((lk - mx) * kLog2e) : 0.f;
+      const float sum = wave_sum(e);
+      L = mx + __logf(sum);
+      const float w = e / sum;                                      // exp(LSE_k - LSE)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) * v[u];
+      for (int j = 8; j < ns; j += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = j + u < ns ? *(const f32x4*)(src + (j + u) * piece) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u)) * v[u];
+      }
+    }
+  } else {
+    // more than 64 pieces: the LSEs are reduced in groups of 64
+    float mx = -INFINITY;
+    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, lse_k[(int64_t)k * p.rows]);
+    mx = wave_max(mx);
+    if (mx != -INFINITY) {
+      float sum = 0.f;
+      for (int k = lane; k < ns; k += 64) sum += __builtin_amdgcn_exp2f((lse_k[(int64_t)k * p.rows] - mx) * kLog2e);
+      sum = wave_sum(sum);
+      L = mx + __logf(sum);
+      for (int k0 = 0; k0 < ns; k0 += 64) {
+        const int kl = k0 + lane;
+        const float w = kl < ns ? __builtin_amdgcn_exp2f((lse_k[(int64_t)kl * p.rows] - L) * kLog2e) : 0.f;
+        const int n = min(64, ns - k0);
+        for (int j = 0; j < n; j += 8) {
+          f32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = j + u < n ? *(const f32x4*)(src + (k0 + j + u) * piece) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u)) * v[u];
+        }
+      }
     }
   }
-  u32x4 wv = {Dt<T>::pack2(acc0[0], acc0[1]), Dt<T>::pack2(acc0[2], acc0[3]),
-              Dt<T>::pack2(acc1[0], acc1[1]), Dt<T>::pack2(acc1[2], acc1[3])};
-  *(u32x4*)dst = wv;
-  if (lane == 0) *lse_dst = L;
+  const int tok = row / p.h_q;
+  const int head = row - tok * p.h_q;
+  T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + col;
+  *(u32x2*)dst = u32x2{Dt<T>::pack2(acc[0], acc[1]), Dt<T>::pack2(acc[2], acc[3])};
+  if (blockIdx.z == 0 && lane == 0) p.lse[(int64_t)b * p.rows + row] = L;
 }
 
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st) {
-  dim3 grid(p.batch, (p.rows + 3) / 4);
+  dim3 grid(p.batch, (p.rows + 3) / 4, 2);
   if (dtype == 0) hipLaunchKernelGGL(combine_kernel<__bf16>, grid, dim3(256), 0, st, p);
   else hipLaunchKernelGGL(combine_kernel<_Float16>, grid, dim3(256), 0, st, p);
   return hipGetLastError();
