@@ -56,13 +56,15 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 #define MLA_D_K 576             /* cached row width = query width           */
 #define MLA_D_V 512             /* value width: the first 512 columns       */
 #define MLA_PAGE_SIZE 64        /* tokens per KV-cache page                 */
 #define MLA_SCHED_FIELDS 8      /* int32 per scheduler partition            */
 #define MLA_FIXED_OVERHEAD 5    /* per-piece overhead, in pages (scheduler) */
+#define MLA_FUSED_MAX_PIECES 4  /* mla_decode_fused merges requests cut into */
+                                /* at most this many pieces in its first kernel */
 
 typedef enum {
   MLA_SUCCESS = 0,
@@ -128,9 +130,12 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, in
                             int num_parts, int32_t* sched, int32_t* split_offsets, void* stream);
 
 /*
- * Bytes of device workspace mla_decode needs: fp32 partial outputs and LSEs for
- * up to (batch + num_parts) request pieces of s_q*h_q rows each
- * ((batch + num_parts) * s_q * h_q * (512 + 1) * 4 bytes, rounded up to 256).
+ * Bytes of device workspace the decode entry points need: first the arrival
+ * counters of mla_decode_fused (m_blocks * batch int32, rounded up to 256 bytes;
+ * m_blocks = ceil(s_q*h_q / 64), or 1 when s_q*h_q <= 16), then fp32 partial
+ * outputs and LSEs for up to (batch + num_parts) request pieces of s_q*h_q
+ * rows each ((batch + num_parts) * s_q * h_q * (512 + 1) * 4 bytes, rounded up
+ * to 256).
  * Errors: INVALID_VALUE.
  */
 mla_status mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes);
@@ -193,6 +198,26 @@ mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream);
  * Same arguments and errors as mla_decode.
  */
 mla_status mla_decode_combine(const mla_decode_args* args, void* stream);
+
+/*
+ * Paged MLA decode with the combine folded into the split-KV kernel (the
+ * counterpart of starting the combine kernel early by programmatic dependent
+ * launch: page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析", section
+ * "辅助优化：可编程依赖启动与瓦片调度").  Same result and arguments as mla_decode.
+ * A workgroup that stores a piece of a split request counts itself in on a
+ * device-scope atomic counter in the workspace; the one that stores the last
+ * piece of a row tile merges the tile's pieces by their LSE and writes out/lse.
+ * This is done for requests cut into at most MLA_FUSED_MAX_PIECES pieces; the
+ * combine kernel, launched next on `stream`, merges the others and skips these.
+ * Workspace: the counter region (its first bytes, see mla_workspace_size) must
+ * be zero before the first call on a workspace and again whenever batch or
+ * s_q*h_q grows (e.g. allocate it zero-filled); every call that runs to
+ * completion leaves it zero.  Two calls sharing one workspace must not run
+ * concurrently.  mla_decode, mla_decode_splitkv and mla_decode_combine never
+ * read or write the counters.
+ * Errors: as mla_decode.
+ */
+mla_status mla_decode_fused(const mla_decode_args* args, void* stream);
 
 #ifdef __cplusplus
 }

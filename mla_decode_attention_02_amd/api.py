@@ -75,7 +75,7 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.mla_get_metadata.argtypes = [p, i, i, i, i, i, p, p, p]
     L.mla_workspace_size.restype = st
     L.mla_workspace_size.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
-    for name in ("mla_decode", "mla_decode_splitkv", "mla_decode_combine"):
+    for name in ("mla_decode", "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused"):
         fn = getattr(L, name)
         fn.restype = st
         fn.argtypes = [ctypes.POINTER(DecodeArgs), p]
@@ -194,7 +194,9 @@ class DecodeBuffers:
         self.out = torch.empty((B, s_q, h_q, D_V), dtype=q.dtype, device=q.device)
         self.lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
         nbytes = workspace_size(B, s_q, h_q, num_parts)
-        self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+        # zero-filled: the fused path's arrival counters must start at zero
+        # (every completed call leaves them zero again)
+        self.workspace = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
 
 
 def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
@@ -218,6 +220,18 @@ def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor
     lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result
     (computed here when omitted); `buffers` lets a caller reuse outputs."""
     return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers)
+
+
+def mla_decode_fused(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                     cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
+                     metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                     buffers: Optional[DecodeBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged MLA decode with the merge of split requests (up to 4 pieces) done
+    inside the split-KV kernel; same result as mla_decode.  `buffers` must come
+    from DecodeBuffers (zero-filled workspace) and not be shared by two calls
+    in flight on different streams."""
+    return _call("mla_decode_fused", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata,
+                 buffers)
 
 
 def mla_decode_splitkv(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):

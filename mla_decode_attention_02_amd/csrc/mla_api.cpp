@@ -16,6 +16,8 @@
 #include "mla_common.hpp"
 #include "mla_internal.h"
 
+static_assert(mla::kFusedMaxPieces == MLA_FUSED_MAX_PIECES, "fused-merge limit");
+
 namespace {
 
 thread_local std::string g_error;
@@ -50,11 +52,22 @@ mla_status check_shape(int batch, int s_q, int h_q, int h_kv) {
   return MLA_SUCCESS;
 }
 
+// Workspace: the arrival counters of the fused merge [m_blocks, batch] int32
+// first (their place depends on the shape only, not on num_parts), then fp32
+// partial outputs [slots, rows, 512] and their LSEs [slots, rows]; each region
+// starts on a 256-byte boundary.
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t counters_bytes(int batch, int s_q, int h_q) {
+  const int rows = s_q * h_q;
+  const size_t m_blocks = (size_t)((rows + tile_rows(rows) - 1) / tile_rows(rows));
+  return round256(m_blocks * (size_t)batch * sizeof(int32_t));
+}
+
 size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
   const size_t slots = (size_t)batch + (size_t)num_parts;
   const size_t rows = (size_t)s_q * h_q;
-  const size_t bytes = slots * rows * (mla::kDV + 1) * sizeof(float);
-  return (bytes + 255) / 256 * 256;
+  return counters_bytes(batch, s_q, h_q) + round256(slots * rows * (mla::kDV + 1) * sizeof(float));
 }
 
 mla_status check_decode(const mla_decode_args* a) {
@@ -124,8 +137,10 @@ mla::DecodeParams make_params(const mla_decode_args* a) {
   p.o_s0 = a->out_stride[0]; p.o_s1 = a->out_stride[1]; p.o_s2 = a->out_stride[2];
   p.lse = a->lse;
   const size_t slots = (size_t)a->batch + (size_t)a->num_parts;
-  p.part_o = static_cast<float*>(a->workspace);
+  p.counters = static_cast<int*>(a->workspace);
+  p.part_o = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + counters_bytes(a->batch, a->s_q, a->h_q));
   p.part_lse = p.part_o + slots * (size_t)p.rows * mla::kDV;
+  p.fuse_max = 0;
   return p;
 }
 
@@ -189,10 +204,9 @@ mla_status mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t
   return ok();
 }
 
-mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream) {
-  mla_status st = check_decode(args);
-  if (st != MLA_SUCCESS) return st;
-  const mla::DecodeParams p = make_params(args);
+namespace {
+
+mla_status launch_splitkv(const mla_decode_args* args, const mla::DecodeParams& p, void* stream) {
   const int tile = tile_rows(p.rows);
   const int m_blocks = (p.rows + tile - 1) / tile;
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -202,19 +216,40 @@ mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream) {
   return ok();
 }
 
-mla_status mla_decode_combine(const mla_decode_args* args, void* stream) {
-  mla_status st = check_decode(args);
-  if (st != MLA_SUCCESS) return st;
-  const mla::DecodeParams p = make_params(args);
+mla_status launch_combine(const mla_decode_args* args, const mla::DecodeParams& p, void* stream) {
   hipError_t e = mla::launch_combine(p, args->dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
+}
+
+}  // namespace
+
+mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream) {
+  mla_status st = check_decode(args);
+  if (st != MLA_SUCCESS) return st;
+  return launch_splitkv(args, make_params(args), stream);
+}
+
+mla_status mla_decode_combine(const mla_decode_args* args, void* stream) {
+  mla_status st = check_decode(args);
+  if (st != MLA_SUCCESS) return st;
+  return launch_combine(args, make_params(args), stream);
 }
 
 mla_status mla_decode(const mla_decode_args* args, void* stream) {
   mla_status st = mla_decode_splitkv(args, stream);
   if (st != MLA_SUCCESS) return st;
   return mla_decode_combine(args, stream);
+}
+
+mla_status mla_decode_fused(const mla_decode_args* args, void* stream) {
+  mla_status st = check_decode(args);
+  if (st != MLA_SUCCESS) return st;
+  mla::DecodeParams p = make_params(args);
+  p.fuse_max = mla::kFusedMaxPieces;
+  st = launch_splitkv(args, p, stream);
+  if (st != MLA_SUCCESS) return st;
+  return launch_combine(args, p, stream);
 }
 
 }  // extern "C"

@@ -9,8 +9,8 @@
 // are already in flight; the weighted sum keeps eight pieces' loads in flight
 // per lane, so a request cut into many pieces is not a chain of dependent
 // memory round trips.  Requests with no cached token get
-// O = 0 and LSE = -inf; whole (unsplit) requests were already written by the
-// split-KV kernel and are skipped.
+// O = 0 and LSE = -inf; whole (unsplit) requests, and split requests the
+// split-KV kernel merged itself (at most fuse_max pieces), are skipped.
 #include "mla_common.hpp"
 #include "mla_internal.h"
 
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
   if (row >= p.rows) return;
   const int s0 = ldu(p.split_offsets + b);
   const int ns = ldu(p.split_offsets + b + 1) - s0;
-  if (ns == 1) return;
+  if (ns == 1 || (ns > 1 && ns <= p.fuse_max)) return;   // whole, or merged by the split-KV kernel
   const float* lse_k = p.part_lse + (int64_t)s0 * p.rows + row;   // stride p.rows per piece
 
   const float* src = p.part_o + ((int64_t)s0 * p.rows + row) * kDV + col;

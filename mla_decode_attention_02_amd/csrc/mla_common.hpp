@@ -56,6 +56,9 @@ struct DecodeParams {
   float* lse;               // [batch * rows]
   float* part_o;            // [slots, rows, 512] fp32
   float* part_lse;          // [slots, rows]
+  int* counters;            // [m_blocks, batch] arrivals per row tile of a split request
+  int fuse_max;             // requests cut into 2 .. fuse_max pieces are merged in the
+                            // split-KV kernel (0: never)
 };
 
 // ---------------------------------------------------------------- dtypes --

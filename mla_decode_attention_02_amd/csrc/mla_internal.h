@@ -8,12 +8,16 @@ namespace mla {
 
 struct DecodeParams;
 
+// Split requests cut into at most this many pieces are merged inside the
+// split-KV kernel on the fused path.
+constexpr int kFusedMaxPieces = 4;
+
 // Split-KV attention, 64-row tiles: grid (num_parts, m_blocks), 512 threads.
 // dtype 0 = bf16, 1 = fp16.
 hipError_t launch_splitkv_wide(const DecodeParams& p, int dtype, int m_blocks, hipStream_t st);
 // Split-KV attention, one tile of up to 16 rows: grid (num_parts), 256 threads.
 hipError_t launch_splitkv_narrow(const DecodeParams& p, int dtype, hipStream_t st);
-// Merge of split pieces: grid (batch, ceil(rows / 4)), 256 threads.
+// Merge of split pieces: grid (batch, ceil(rows / 4), 2 column halves), 256 threads.
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st);
 // Tile schedule: one workgroup.
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead,

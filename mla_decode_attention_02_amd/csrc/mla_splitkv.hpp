@@ -86,6 +86,97 @@ __device__ __forceinline__ BufRsrc page_of(const DecodeParams& p, int phys, int 
   return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0 * 2, page_bytes);
 }
 
+// --------------------------------------------------------- fused merge --
+// The combine folded into the split-KV kernel (the MI355X answer to launching
+// the combine kernel early, page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析",
+// section "辅助优化：可编程依赖启动与瓦片调度"): after a workgroup has written its
+// piece of a split request, it counts itself in with a device-scope atomic, and
+// the workgroup that writes the last piece of a row tile merges all of that
+// tile's pieces by their LSE, LSE = log sum_k exp(LSE_k) and
+// O = sum_k exp(LSE_k - LSE) O_k, then resets the counter for the next call.
+// Used for requests cut into at most kFusedMaxPieces pieces: the merging
+// workgroup reads every piece of its tile, which only pays while they are few.
+// LDS of the merge: weights of the pieces per tile row, and the "last" flag.
+template <int kRowsTile>
+struct MergeLds {
+  float w[kFusedMaxPieces][kRowsTile];
+  int last;
+};
+
+// Called by every thread of the workgroup (it holds barriers) after the
+// workgroup's piece (c.split of request c.b, tile rows row0 ..) was stored.
+template <typename T, int kRowsTile, int kNThreads>
+__device__ __forceinline__ void fused_merge(const DecodeParams& p, const Chunk& c, int row0,
+                                            MergeLds<kRowsTile>& m) {
+  const int tid = threadIdx.x;
+  // Every wave waits for its own piece stores; then one thread makes them
+  // visible device-wide (one release: a fence per thread would write back and
+  // invalidate the cache once per wave) and counts the workgroup in.  The
+  // workgroup that arrives last acquires the other pieces' stores.
+  __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+  __syncthreads();
+  int* ctr = p.counters + (int64_t)blockIdx.y * p.batch + c.b;
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = atomicAdd(ctr, 1) == c.nsplit - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    m.last = last;
+  }
+  __syncthreads();
+  if (!m.last) return;                              // uniform over the workgroup
+  const int ns = c.nsplit;
+  const int64_t s0 = c.slot0;
+  if (tid < kRowsTile) {
+    const int row = row0 + tid;
+    float lk[kFusedMaxPieces];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFusedMaxPieces; ++k) {
+      lk[k] = (k < ns && row < p.rows) ? p.part_lse[(s0 + k) * p.rows + row] : -INFINITY;
+      mx = fmaxf(mx, lk[k]);
+    }
+    float e[kFusedMaxPieces], sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kFusedMaxPieces; ++k) {
+      e[k] = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lk[k] - mx) * kLog2e);
+      sum += e[k];
+    }
+    const float inv = mx == -INFINITY ? 0.f : 1.f / sum;
+#pragma unroll
+    for (int k = 0; k < kFusedMaxPieces; ++k) m.w[k][tid] = e[k] * inv;   // exp(LSE_k - LSE)
+    if (row < p.rows) p.lse[(int64_t)c.b * p.rows + row] = mx == -INFINITY ? -INFINITY : mx + __logf(sum);
+  }
+  __syncthreads();
+  // (row, 4-column) items, eight per batch and thread; every piece's loads of a
+  // batch are in flight together (absent pieces reread the last one, weight 0)
+  constexpr int kItems = kRowsTile * (kDV / 4) / kNThreads;
+  static_assert(kItems % 8 == 0, "items per thread come in batches of eight");
+#pragma unroll 1
+  for (int ib = 0; ib < kItems; ib += 8) {
+    f32x4 v[kFusedMaxPieces][8];
+#pragma unroll
+    for (int k = 0; k < kFusedMaxPieces; ++k) {
+      const int64_t slot = s0 + min(k, ns - 1);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int it = tid + (ib + u) * kNThreads;
+        const int row = min(row0 + (it >> 7), p.rows - 1);
+        v[k][u] = *(const f32x4*)(p.part_o + (slot * p.rows + row) * kDV + (it & 127) * 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int it = tid + (ib + u) * kNThreads;
+      const int rl = it >> 7;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kFusedMaxPieces; ++k) acc += m.w[k][rl] * v[k][u];
+      if (row0 + rl < p.rows) store_out4<T>(p, c.b, row0 + rl, (it & 127) * 4, acc);
+    }
+  }
+  if (tid == 0) *ctr = 0;                           // every piece has arrived: ready for the next call
+}
+
 // Cache policy of page loads: the narrow kernel reads every page once; in the
 // wide kernel the row tiles of one request read the same pages and may meet in L2.
 constexpr int kNarrowAux = 2;

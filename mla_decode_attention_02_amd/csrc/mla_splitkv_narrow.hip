@@ -12,6 +12,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
   __shared__ __attribute__((aligned(1024))) char kbuf1_raw[kPageBytes];
   __shared__ float m_w[kWaves][16];
   __shared__ float l_w[kWaves][16];
+  __shared__ MergeLds<16> merge_s;
   MLA_LDS char* kbuf0 = (MLA_LDS char*)kbuf0_raw;
   MLA_LDS char* kbuf1 = (MLA_LDS char*)kbuf1_raw;
   constexpr int kMergeStride = kDV + 4;   // floats per row of the merge buffer
@@ -154,6 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
       else p.part_lse[(int64_t)(c.slot0 + c.split) * p.rows + tid] = lse;
     }
     lds_barrier();
+    if (c.nsplit > 1 && c.nsplit <= p.fuse_max) fused_merge<T, 16, kThreads>(p, c, 0, merge_s);
   });
 }
 

@@ -34,6 +34,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   __shared__ float alpha_s[2][64];
   __shared__ float l_s[64];
   __shared__ float m_s[64];
+  __shared__ MergeLds<64> merge_s;
   auto hbuf = [&](auto ic) -> MLA_LDS char* {
     constexpr int i = decltype(ic)::value & 3;
     if constexpr (i == 0) return (MLA_LDS char*)hb0_raw;
@@ -186,6 +187,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         }
       }
       lds_barrier();                                                        // X(nh)
+      if (c.nsplit > 1 && c.nsplit <= p.fuse_max) fused_merge<T, 64, 512>(p, c, mrow0, merge_s);
     });
   } else {
     // ------------------------------------------------------- output waves --
@@ -276,6 +278,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
           if (cw == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
         }
       }
+      if (c.nsplit > 1 && c.nsplit <= p.fuse_max) fused_merge<T, 64, 512>(p, c, mrow0, merge_s);
     });
   }
 }

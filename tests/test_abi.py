@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mla_last_error", "mla_abi_version", "mla_get_metadata_shape", "mla_get_metadata",
-              "mla_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine"):
+              "mla_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
+              "mla_decode_fused"):
         assert n in names
 
 
@@ -44,15 +45,19 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.mla_abi_version() == 1
+    assert L.mla_abi_version() == 2
     assert L.mla_last_error() is not None
 
 
 def test_workspace_size_formula(L):
     for batch, s_q, h_q, parts in ((2, 1, 16, 256), (64, 1, 128, 128), (32, 2, 128, 64), (1, 1, 1, 1)):
         n = api.workspace_size(batch, s_q, h_q, parts)
+        # the fused path's counters (one per request and 64-row tile, or per
+        # request when s_q*h_q <= 16), then partials and LSEs
         raw = (batch + parts) * s_q * h_q * 513 * 4
-        assert n == (raw + 255) // 256 * 256
+        rows = s_q * h_q
+        m_blocks = 1 if rows <= 16 else (rows + 63) // 64
+        assert n == (raw + 255) // 256 * 256 + (m_blocks * batch * 4 + 255) // 256 * 256
 
 
 def test_metadata_shape_with_explicit_cu_count(L):
@@ -145,7 +150,7 @@ BREAKS = [
 
 
 @pytest.mark.parametrize("name,brk,status", BREAKS, ids=[b[0] for b in BREAKS])
-@pytest.mark.parametrize("entry", ["mla_decode", "mla_decode_splitkv", "mla_decode_combine"])
+@pytest.mark.parametrize("entry", ["mla_decode", "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused"])
 def test_decode_rejects_bad_arguments(L, entry, name, brk, status):
     a = _valid_args()
     brk(a)

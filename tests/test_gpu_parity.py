@@ -37,12 +37,15 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def run(x, num_parts=None):
+ENTRIES = ["mla_decode", "mla_decode_fused"]
+
+
+def run(x, num_parts=None, entry="mla_decode", buffers=None):
     dev = torch.device("cuda:0")
     g = x.to(dev)
     meta = api.get_metadata(g.cache_seqlens, g.q.shape[1], g.q.shape[2], num_parts=num_parts)
-    out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale,
-                              g.causal, metadata=meta)
+    out, lse = getattr(api, entry)(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale,
+                                   g.causal, metadata=meta, buffers=buffers)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), [m.cpu().numpy() for m in meta]
 
@@ -114,22 +117,24 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("s_q,h_q,seqlens,causal,dtype,parts", EDGE,
                          ids=[f"sq{c[0]}_hq{c[1]}_{'c' if c[3] else 'n'}_{c[4]}_p{c[5]}" for c in EDGE])
-def test_small_parity(s_q, h_q, seqlens, causal, dtype, parts):
-    tag = f"small s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {dtype} parts={parts}"
+def test_small_parity(s_q, h_q, seqlens, causal, dtype, parts, entry):
+    tag = f"small {entry} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {dtype} parts={parts}"
     _say(tag)
     x = make_inputs(len(seqlens), s_q, h_q, dtype, seqlens=seqlens, causal=causal,
                     seed=sum(seqlens) + h_q, poison=True, extra_pages=3)
-    out, lse, _ = run(x, parts)
+    out, lse, _ = run(x, parts, entry)
     ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, causal)
     compare(out, lse, ref_o, ref_l, tag)
 
 
-def test_empty_request_and_masked_rows():
-    _say("empty request / fully masked causal rows")
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_empty_request_and_masked_rows(entry):
+    _say(f"empty request / fully masked causal rows ({entry})")
     x = make_inputs(3, 3, 16, "bf16", seqlens=(0, 1, 70), causal=True, seed=5, poison=True)
-    out, lse, _ = run(x, 2)
+    out, lse, _ = run(x, 2, entry)
     ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, True)
     compare(out, lse, ref_o, ref_l, "empty")
     assert np.all(np.isneginf(lse[0])) and not out[0].any()
@@ -209,15 +214,41 @@ def test_split_counts_agree(h_q):
     assert np.abs(l1 - l2).max() <= 1e-4
 
 
+# ------------------------------------------------------------ fused path --
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fused_repeated_calls_reuse_counters(h_q):
+    """The fused merge's arrival counters live in the workspace: consecutive
+    calls with different piece counts on one set of buffers agree with the
+    two-kernel path, and leave the counters at zero."""
+    dev = torch.device("cuda:0")
+    parts = 17
+    cases = [(900, 33, 2000, 640, 1), (300, 5000, 64, 64, 2), (1, 2, 3, 4000, 700)]
+    bufs = None
+    for i, seqlens in enumerate(cases):
+        _say(f"fused repeated call {i} h_q={h_q} seqlens={seqlens} parts={parts}")
+        x = make_inputs(len(seqlens), 1, h_q, "bf16", seqlens=seqlens, seed=40 + i)
+        if bufs is None:
+            bufs = api.DecodeBuffers(x.q.to(dev), parts)
+        o_ref, l_ref, meta = run(x, parts, "mla_decode")
+        assert (np.diff(meta[1]) > 1).any(), "expected split requests"
+        o_f, l_f, _ = run(x, parts, "mla_decode_fused", buffers=bufs)
+        # the two merges round differently in fp32: at most one bf16 step apart
+        assert np.all(np.abs(o_f - o_ref) <= 2.0 ** -7 * np.abs(o_ref) + 1e-6)
+        assert np.abs(l_f - l_ref).max() <= 1e-5
+        # the counters are the first 256 bytes of this workspace (5 requests)
+        assert not bufs.workspace[:256].any(), "arrival counters were not reset"
+
+
 # ----------------------------------------------------- full-size samples --
+@pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_workload_full_size_sampled(idx):
+def test_workload_full_size_sampled(idx, entry):
     """Full-size workload in the launch configuration the benchmark uses;
     the oracle checks a sample of requests (first, last, and the longest)."""
     w = WORKLOADS[idx]
-    _say(f"workload {idx} {w.name} full size")
+    _say(f"workload {idx} {w.name} full size ({entry})")
     x = workload_inputs(idx)
-    out, lse, meta = run(x)
+    out, lse, meta = run(x, entry=entry)
     seqlens = x.cache_seqlens.tolist()
     offs = meta[1]
     split = [b for b in range(w.batch) if offs[b + 1] - offs[b] > 1]
