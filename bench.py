@@ -208,8 +208,8 @@ def cpu_baseline(inputs, seconds: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, help="1..5; 2 is the headline workload")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -3,7 +3,8 @@
 // combine kernel that follows splitkv_mla).  For a request cut into pieces k
 // with normalised partial outputs O_k and LSE_k:
 //   LSE = log sum_k exp(LSE_k),   O = sum_k exp(LSE_k - LSE) * O_k.
-// One wave per (query row, half of the 512 columns); each lane owns 4 columns.
+// One wave per query row, or per half row when rows are few; each lane owns 8
+// or 4 columns.
 // The lanes load the pieces' LSEs together (lane k holds piece k of a group of
 // 64) and reduce them across the wave, while the first eight pieces' data loads
 // are already in flight; the weighted sum keeps eight pieces' loads in flight
@@ -28,7 +29,9 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <typename T>
+// kCh = 16-byte column chunks per lane and piece: 1 (a wave covers half of
+// the 512 columns) or 2 (the whole row, chunks 256 floats apart).
+template <typename T, int kCh>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -42,13 +45,29 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
 
   const float* src = p.part_o + ((int64_t)s0 * p.rows + row) * kDV + col;
   const int64_t piece = (int64_t)p.rows * kDV;                      // floats between pieces
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kCh];
+#pragma unroll
+  for (int h = 0; h < kCh; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = -INFINITY;
+  auto load8 = [&](f32x4 (&v)[8][kCh], int k0, int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int h = 0; h < kCh; ++h)
+        v[u][h] = k0 + u < n ? *(const f32x4*)(src + (k0 + u) * piece + h * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto acc8 = [&](const f32x4 (&v)[8][kCh], float w, int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j0 + u));
+#pragma unroll
+      for (int h = 0; h < kCh; ++h) acc[h] += wu * v[u][h];
+    }
+  };
   if (ns <= 64) {
     // the first eight pieces' data loads go out together with the LSE loads
-    f32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = u < ns ? *(const f32x4*)(src + u * piece) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 v[8][kCh];
+    load8(v, 0, ns);
     const float lk = lane < ns ? lse_k[(int64_t)lane * p.rows] : -INFINITY;
     const float mx = wave_max(lk);
     if (mx != -INFINITY) {
@@ -56,13 +75,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
       const float sum = wave_sum(e);
       L = mx + __logf(sum);
       const float w = e / sum;                                      // exp(LSE_k - LSE)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) * v[u];
+      acc8(v, w, 0);
       for (int j = 8; j < ns; j += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = j + u < ns ? *(const f32x4*)(src + (j + u) * piece) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u)) * v[u];
+        load8(v, j, ns);
+        acc8(v, w, j);
       }
     }
   } else {
@@ -80,11 +96,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
         const float w = kl < ns ? __builtin_amdgcn_exp2f((lse_k[(int64_t)kl * p.rows] - L) * kLog2e) : 0.f;
         const int n = min(64, ns - k0);
         for (int j = 0; j < n; j += 8) {
-          f32x4 v[8];
+          f32x4 v[8][kCh];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = j + u < n ? *(const f32x4*)(src + (k0 + j + u) * piece) : f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u)) * v[u];
+            for (int h = 0; h < kCh; ++h)
+              v[u][h] = j + u < n ? *(const f32x4*)(src + (k0 + j + u) * piece + h * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
+          acc8(v, w, j);
         }
       }
     }
@@ -92,14 +110,24 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
   const int tok = row / p.h_q;
   const int head = row - tok * p.h_q;
   T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + col;
-  *(u32x2*)dst = u32x2{Dt<T>::pack2(acc[0], acc[1]), Dt<T>::pack2(acc[2], acc[3])};
+#pragma unroll
+  for (int h = 0; h < kCh; ++h)
+    *(u32x2*)(dst + h * 256) = u32x2{Dt<T>::pack2(acc[h][0], acc[h][1]), Dt<T>::pack2(acc[h][2], acc[h][3])};
   if (blockIdx.z == 0 && lane == 0) p.lse[(int64_t)b * p.rows + row] = L;
 }
 
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st) {
-  dim3 grid(p.batch, (p.rows + 3) / 4, 2);
-  if (dtype == 0) hipLaunchKernelGGL(combine_kernel<__bf16>, grid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL(combine_kernel<_Float16>, grid, dim3(256), 0, st, p);
+  // whole rows per wave when there are enough rows to fill the chip, else
+  // half rows (twice the waves)
+  const bool whole = (int64_t)p.batch * p.rows >= 4096;
+  dim3 grid(p.batch, (p.rows + 3) / 4, whole ? 1 : 2);
+  if (dtype == 0) {
+    if (whole) hipLaunchKernelGGL((combine_kernel<__bf16, 2>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((combine_kernel<__bf16, 1>), grid, dim3(256), 0, st, p);
+  } else {
+    if (whole) hipLaunchKernelGGL((combine_kernel<_Float16, 2>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((combine_kernel<_Float16, 1>), grid, dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 
