@@ -219,6 +219,44 @@ mla_status mla_decode_combine(const mla_decode_args* args, void* stream);
  */
 mla_status mla_decode_fused(const mla_decode_args* args, void* stream);
 
+/* Arguments of mla_merge_partials.  Strides are in ELEMENTS; the innermost
+ * (feature) dimension of part_out and out must be contiguous. */
+typedef struct {
+  int dtype;                   /* mla_dtype of part_out and out               */
+  int num_shards;              /* >= 1                                        */
+  int batch, s_q, h_q;
+  const void* part_out;        /* device: shard r's out, [num_shards][batch, s_q, h_q, 512] */
+  int64_t part_out_stride[4];  /*   strides of shard, batch, token, head      */
+  const float* part_lse;       /* device: shard r's lse, [num_shards][batch, s_q, h_q] fp32 */
+  int64_t part_lse_stride;     /*   stride between shards (contiguous within) */
+  void* out;                   /* device [batch, s_q, h_q, 512], dtype        */
+  int64_t out_stride[3];       /*   strides of batch, token, head             */
+  float* lse;                  /* device [batch, s_q, h_q] fp32, contiguous   */
+} mla_merge_args;
+
+/*
+ * Merge of context-parallel shards (the one-GPU part of splitting a request's
+ * cached tokens over several GPUs, each running mla_decode on its own range):
+ * for every (b, i, h), with shard results O_r = out_r[b,i,h,:] and L_r =
+ * lse_r[b,i,h],
+ *     LSE = log sum_r exp(L_r),   O = sum_r exp(L_r - LSE) * O_r
+ * -- the merge the combine kernel applies to the pieces of a split request
+ * (page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析", section
+ * "辅助优化：可编程依赖启动与瓦片调度").  Shards with L_r = -inf contribute
+ * nothing; if every shard has -inf, O = 0 and LSE = -inf.
+ * Causal masking with s_q > 1 is bottom-right aligned over the whole request,
+ * so a shard that holds the request's last cached tokens runs mla_decode with
+ * causal = 1 and its own length, and every other shard must end at or before
+ * token n - s_q + 1 (all of its keys visible to every new token) and runs with
+ * causal = 0.
+ * Alignment: part_out and out 16-byte aligned, their strides multiples of 8;
+ * part_lse and lse 4-byte aligned.  Nothing is allocated; the call only
+ * enqueues one kernel on `stream`.
+ * Errors: INVALID_VALUE (null pointer, non-positive size, bad stride or
+ * alignment), UNSUPPORTED (dtype), HIP (launch failed).
+ */
+mla_status mla_merge_partials(const mla_merge_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

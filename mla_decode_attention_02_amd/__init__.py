@@ -7,7 +7,8 @@ and raises if the library has not been built.
 """
 
 __all__ = ["get_metadata", "get_metadata_shape", "workspace_size", "mla_decode",
-           "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused", "library_path"]
+           "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused", "mla_merge_partials",
+           "library_path"]
 
 
 def __getattr__(name):

@@ -35,6 +35,19 @@ class MlaError(RuntimeError):
         self.status = status
 
 
+class MergeArgs(ctypes.Structure):
+    """Mirror of mla_merge_args."""
+
+    _fields_ = [
+        ("dtype", ctypes.c_int), ("num_shards", ctypes.c_int),
+        ("batch", ctypes.c_int), ("s_q", ctypes.c_int), ("h_q", ctypes.c_int),
+        ("part_out", ctypes.c_void_p), ("part_out_stride", ctypes.c_int64 * 4),
+        ("part_lse", ctypes.c_void_p), ("part_lse_stride", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64 * 3),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
 class DecodeArgs(ctypes.Structure):
     """Mirror of mla_decode_args."""
 
@@ -79,6 +92,8 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = st
         fn.argtypes = [ctypes.POINTER(DecodeArgs), p]
+    L.mla_merge_partials.restype = st
+    L.mla_merge_partials.argtypes = [ctypes.POINTER(MergeArgs), p]
     return L
 
 
@@ -244,3 +259,39 @@ def mla_decode_combine(q, k_cache, block_table, cache_seqlens, softmax_scale, ca
     """Second phase only (merge of split pieces)."""
     return _call("mla_decode_combine", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
                  metadata, buffers)
+
+
+def mla_merge_partials(part_out: torch.Tensor, part_lse: torch.Tensor,
+                       out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge the results of N context-parallel shards of the same requests:
+    part_out [N, B, s_q, h_q, 512] (bf16/fp16), part_lse [N, B, s_q, h_q] fp32
+    -> (out [B, s_q, h_q, 512], lse [B, s_q, h_q]).  Each shard's pair is what
+    mla_decode returns for that shard's range of cached tokens."""
+    if part_out.dtype not in DTYPE_CODES:
+        raise ValueError("part_out must be bf16 or fp16")
+    if part_out.dim() != 5 or part_out.shape[4] != D_V or part_lse.dim() != 4:
+        raise ValueError("expected part_out [N, B, s_q, h_q, 512] and part_lse [N, B, s_q, h_q]")
+    if tuple(part_lse.shape) != tuple(part_out.shape[:4]) or part_lse.dtype != torch.float32:
+        raise ValueError("part_lse must be fp32 [N, B, s_q, h_q] matching part_out")
+    if not part_lse[0].is_contiguous():
+        raise ValueError("each shard of part_lse must be contiguous")
+    N, B, s_q, h_q, _ = part_out.shape
+    if out is None:
+        out = torch.empty((B, s_q, h_q, D_V), dtype=part_out.dtype, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=part_out.device)
+    a = MergeArgs()
+    a.dtype = DTYPE_CODES[part_out.dtype]
+    a.num_shards, a.batch, a.s_q, a.h_q = N, B, s_q, h_q
+    a.part_out = part_out.data_ptr()
+    for i in range(4):
+        a.part_out_stride[i] = part_out.stride(i)
+    a.part_lse = part_lse.data_ptr()
+    a.part_lse_stride = part_lse.stride(0)
+    a.out = out.data_ptr()
+    for i in range(3):
+        a.out_stride[i] = out.stride(i)
+    a.lse = lse.data_ptr()
+    _check(lib().mla_merge_partials(ctypes.byref(a), _stream_ptr(part_out.device)))
+    return out, lse

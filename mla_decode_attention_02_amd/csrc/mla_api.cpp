@@ -242,6 +242,49 @@ mla_status mla_decode(const mla_decode_args* args, void* stream) {
   return mla_decode_combine(args, stream);
 }
 
+mla_status mla_merge_partials(const mla_merge_args* a, void* stream) {
+  if (!a) return fail(MLA_ERROR_INVALID_VALUE, "args is NULL");
+  if (a->dtype != MLA_DTYPE_BF16 && a->dtype != MLA_DTYPE_FP16)
+    return fail(MLA_ERROR_UNSUPPORTED, "dtype %d is not bf16 (0) or fp16 (1)", a->dtype);
+  if (a->num_shards <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_shards must be positive");
+  mla_status st = check_shape(a->batch, a->s_q, a->h_q, 1);
+  if (st != MLA_SUCCESS) return st;
+  if (!a->part_out || !a->part_lse || !a->out || !a->lse)
+    return fail(MLA_ERROR_INVALID_VALUE, "a required pointer is NULL");
+  if (!aligned(a->part_out, 16) || !aligned(a->out, 16))
+    return fail(MLA_ERROR_INVALID_VALUE, "part_out and out must be 16-byte aligned");
+  if (!aligned(a->part_lse, 4) || !aligned(a->lse, 4))
+    return fail(MLA_ERROR_INVALID_VALUE, "part_lse and lse must be 4-byte aligned");
+  for (int i = 0; i < 4; ++i)
+    if (a->part_out_stride[i] <= 0 || a->part_out_stride[i] % 8)
+      return fail(MLA_ERROR_INVALID_VALUE, "part_out_stride[%d]=%lld must be a positive multiple of 8", i,
+                  (long long)a->part_out_stride[i]);
+  for (int i = 0; i < 3; ++i)
+    if (a->out_stride[i] <= 0 || a->out_stride[i] % 8)
+      return fail(MLA_ERROR_INVALID_VALUE, "out_stride[%d]=%lld must be a positive multiple of 8", i,
+                  (long long)a->out_stride[i]);
+  if (a->part_out_stride[3] < MLA_D_V || a->out_stride[2] < MLA_D_V)
+    return fail(MLA_ERROR_INVALID_VALUE, "head strides must cover a row (>= 512)");
+  const long long rows_total = (long long)a->batch * a->s_q * a->h_q;
+  if (a->part_lse_stride < rows_total)
+    return fail(MLA_ERROR_INVALID_VALUE, "part_lse_stride (%lld) is below batch*s_q*h_q (%lld)",
+                (long long)a->part_lse_stride, rows_total);
+  mla::MergeParams m;
+  m.part_out = a->part_out;
+  m.p_s0 = a->part_out_stride[0]; m.p_s1 = a->part_out_stride[1];
+  m.p_s2 = a->part_out_stride[2]; m.p_s3 = a->part_out_stride[3];
+  m.part_lse = a->part_lse;
+  m.lse_s = a->part_lse_stride;
+  m.num_shards = a->num_shards;
+  m.batch = a->batch; m.s_q = a->s_q; m.h_q = a->h_q;
+  m.out = a->out;
+  m.o_s0 = a->out_stride[0]; m.o_s1 = a->out_stride[1]; m.o_s2 = a->out_stride[2];
+  m.lse = a->lse;
+  hipError_t e = mla::launch_merge(m, a->dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
 mla_status mla_decode_fused(const mla_decode_args* args, void* stream) {
   mla_status st = check_decode(args);
   if (st != MLA_SUCCESS) return st;

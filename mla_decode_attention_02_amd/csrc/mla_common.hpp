@@ -61,6 +61,18 @@ struct DecodeParams {
                             // split-KV kernel (0: never)
 };
 
+// Arguments of the merge of context-parallel shards (strides in elements).
+struct MergeParams {
+  const void* part_out;     // shard r, request b, token, head: r*p_s0 + b*p_s1 + t*p_s2 + h*p_s3
+  int64_t p_s0, p_s1, p_s2, p_s3;
+  const float* part_lse;    // shard r: r*lse_s + b*rows + row
+  int64_t lse_s;
+  int num_shards, batch, s_q, h_q;
+  void* out;
+  int64_t o_s0, o_s1, o_s2;
+  float* lse;               // [batch * rows]
+};
+
 // ---------------------------------------------------------------- dtypes --
 template <typename T> struct Dt;
 
@@ -79,6 +91,11 @@ template <> struct Dt<__bf16> {
     bf16x2 v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // packed pair -> two floats (exact)
+  __device__ static inline void unpack2(uint32_t u, float& x, float& y) {
+    x = __uint_as_float(u << 16);
+    y = __uint_as_float(u & 0xFFFF0000u);
+  }
 };
 
 template <> struct Dt<_Float16> {
@@ -94,6 +111,12 @@ template <> struct Dt<_Float16> {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 v = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline void unpack2(uint32_t u, float& x, float& y) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 v = __builtin_bit_cast(f16x2, u);
+    x = (float)v[0];
+    y = (float)v[1];
   }
 };
 

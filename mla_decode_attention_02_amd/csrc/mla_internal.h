@@ -7,6 +7,7 @@
 namespace mla {
 
 struct DecodeParams;
+struct MergeParams;
 
 // Split requests cut into at most this many pieces are merged inside the
 // split-KV kernel on the fused path.
@@ -19,6 +20,8 @@ hipError_t launch_splitkv_wide(const DecodeParams& p, int dtype, int m_blocks, h
 hipError_t launch_splitkv_narrow(const DecodeParams& p, int dtype, hipStream_t st);
 // Merge of split pieces: grid (batch, ceil(rows / 4), 2 column halves), 256 threads.
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st);
+// Merge of context-parallel shards: grid (batch, ceil(rows / 4)), 256 threads.
+hipError_t launch_merge(const MergeParams& m, int dtype, hipStream_t st);
 // Tile schedule: one workgroup.
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead,
                            int32_t* sched, int32_t* split_offsets, hipStream_t st);

@@ -162,3 +162,48 @@ def test_decode_rejects_bad_arguments(L, entry, name, brk, status):
 def test_null_args_pointer(L):
     assert L.mla_decode(None, None) == INVALID
     assert L.mla_workspace_size(1, 1, 1, 1, None) == INVALID
+
+
+def _valid_merge_args():
+    """A well-formed mla_merge_args block with fake (never dereferenced) device
+    addresses: 3 shards of B=2, s_q=1, h_q=16."""
+    a = api.MergeArgs()
+    a.dtype = 0
+    a.num_shards, a.batch, a.s_q, a.h_q = 3, 2, 1, 16
+    base = 1 << 20
+    a.part_out = base
+    a.part_out_stride[:] = [2 * 16 * 512, 16 * 512, 16 * 512, 512]
+    a.part_lse = base * 2
+    a.part_lse_stride = 2 * 16
+    a.out = base * 3
+    a.out_stride[:] = [16 * 512, 16 * 512, 512]
+    a.lse = base * 4
+    return a
+
+
+MERGE_BREAKS = [
+    ("dtype", lambda a: setattr(a, "dtype", 5), UNSUPPORTED),
+    ("num_shards", lambda a: setattr(a, "num_shards", 0), INVALID),
+    ("batch", lambda a: setattr(a, "batch", 0), INVALID),
+    ("h_q", lambda a: setattr(a, "h_q", -2), INVALID),
+    ("part_out null", lambda a: setattr(a, "part_out", None), INVALID),
+    ("lse null", lambda a: setattr(a, "lse", None), INVALID),
+    ("part_out misaligned", lambda a: setattr(a, "part_out", (1 << 20) + 8), INVALID),
+    ("lse misaligned", lambda a: setattr(a, "lse", 4 * (1 << 20) + 2), INVALID),
+    ("shard stride", lambda a: a.part_out_stride.__setitem__(0, 12), INVALID),
+    ("head stride", lambda a: a.part_out_stride.__setitem__(3, 504), INVALID),
+    ("out stride", lambda a: a.out_stride.__setitem__(1, 0), INVALID),
+    ("lse stride", lambda a: setattr(a, "part_lse_stride", 31), INVALID),
+]
+
+
+@pytest.mark.parametrize("name,brk,status", MERGE_BREAKS, ids=[b[0] for b in MERGE_BREAKS])
+def test_merge_rejects_bad_arguments(L, name, brk, status):
+    a = _valid_merge_args()
+    brk(a)
+    assert L.mla_merge_partials(ctypes.byref(a), None) == status, (name, L.mla_last_error().decode())
+    assert L.mla_last_error().decode() != ""
+
+
+def test_merge_null_args(L):
+    assert L.mla_merge_partials(None, None) == INVALID

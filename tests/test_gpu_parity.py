@@ -262,3 +262,65 @@ def test_workload_full_size_sampled(idx, entry):
         R = w.s_q * w.h_q
         compare(out[b].reshape(R, 512), lse[b].reshape(R), ref_o, ref_l, f"workload {idx} request {b}")
     assert np.isfinite(lse).all()
+
+
+# ------------------------------------------------ context-parallel shards --
+def _shard(x, r, n_shards):
+    """Shard r of every request: pages [r*P//N, (r+1)*P//N) of the request's P
+    pages, as a stand-alone batch (same page pool, its own block table and
+    lengths)."""
+    B = x.block_table.shape[0]
+    bt = torch.full_like(x.block_table, -1)
+    lens = torch.zeros_like(x.cache_seqlens)
+    for b in range(B):
+        n = int(x.cache_seqlens[b])
+        P = (n + 63) // 64
+        lo, hi = r * P // n_shards, (r + 1) * P // n_shards
+        if lo < hi:
+            bt[b, :hi - lo] = x.block_table[b, lo:hi]
+            lens[b] = min(n, hi * 64) - lo * 64
+    return bt, lens
+
+
+@pytest.mark.parametrize("s_q,h_q,n_shards,causal", [(1, 16, 3, False), (1, 128, 4, False),
+                                                     (2, 64, 3, True), (1, 16, 8, False)])
+def test_context_parallel_shards_merge(s_q, h_q, n_shards, causal):
+    """Every shard of the requests runs mla_decode on its own token range (the
+    shard holding the last tokens with the causal mask, the others without);
+    mla_merge_partials of the shard results equals the whole-request oracle."""
+    _say(f"context-parallel merge s_q={s_q} h_q={h_q} shards={n_shards} causal={causal}")
+    seqlens = (1000, 3000, 130, 64)          # 64: one page, so some shards are empty
+    x = make_inputs(len(seqlens), s_q, h_q, "bf16", seqlens=seqlens, causal=causal, seed=51 + h_q,
+                    poison=True)
+    dev = torch.device("cuda:0")
+    g = x.to(dev)
+    outs, lses = [], []
+    for r in range(n_shards):
+        bt, lens = _shard(x, r, n_shards)
+        bt, lens = bt.to(dev), lens.to(dev)
+        last = r == n_shards - 1
+        o, l = api.mla_decode(g.q, g.k_cache, bt, lens, g.softmax_scale, causal and last)
+        outs.append(o.clone())
+        lses.append(l.clone())
+    part_out = torch.stack(outs)
+    part_lse = torch.stack(lses)
+    out, lse = api.mla_merge_partials(part_out, part_lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "context-parallel merge")
+    whole_o, whole_l, _ = run(x)
+    assert np.abs(out.float().cpu().numpy() - whole_o).max() <= 1e-2
+    assert np.abs(lse.cpu().numpy() - whole_l).max() <= 1e-4
+
+
+def test_merge_all_shards_empty():
+    """Rows that no shard saw: O = 0, LSE = -inf."""
+    _say("merge of shards that saw no key")
+    dev = torch.device("cuda:0")
+    part_out = torch.randn(3, 2, 1, 16, 512, device=dev).to(torch.bfloat16)
+    part_lse = torch.full((3, 2, 1, 16), float("-inf"), device=dev)
+    part_lse[1, 1] = 0.5
+    out, lse = api.mla_merge_partials(part_out, part_lse)
+    torch.cuda.synchronize()
+    assert torch.isneginf(lse[0]).all() and not out[0].any()
+    assert torch.allclose(out[1].float(), part_out[1, 1].float()) and torch.allclose(lse[1], part_lse[1, 1])
