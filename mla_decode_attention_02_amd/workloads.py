@@ -22,6 +22,13 @@ Recipe (fixed so that every run reproduces the same tensors):
   request's last page, and every page no request uses, are overwritten with
   +-POISON along the sign of the request's first query row, so that any read of
   them would dominate the softmax and the output.
+  fp8 cache (kv_dtype="fp8", bf16 q only): step 4's fp32 k (poisoned as above)
+  is encoded per page as fp8 e4m3fn codes and one fp32 scale per page:
+    amax_p = max |k[p]|, scale_p = amax_p / 448 ("amax"), or the power of two
+    2^ceil(log2(amax_p / 448)) ("pow2"), or no scale tensor at all ("none",
+    codes = k cast directly); codes = clamp(k / scale_p, +-448) cast with
+    torch's float8_e4m3fn rounding.  The codes and scales are the inputs; the
+    values they stand for are code value * scale_p.
 """
 
 from __future__ import annotations
@@ -37,6 +44,7 @@ PAGE = 64
 POISON = 64.0
 
 _DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+FP8_MAX = 448.0
 
 
 @dataclass(frozen=True)
@@ -53,6 +61,7 @@ class Workload:
     seqlens: Optional[Sequence[int]] = None      # fixed lengths, or
     seqlen_range: Optional[tuple] = None          # inclusive (lo, hi) uniform integers
     seed: int = 0
+    kv: str = "same"                              # "same" (dtype) or "fp8" (e4m3 codes + page scales)
     description: str = field(default="", compare=False)
 
     @property
@@ -60,7 +69,8 @@ class Workload:
         return self.s_q * self.h_q
 
 
-# The five workloads the measurements are quoted on.  Seeds are the index.
+# The workloads the measurements are quoted on.  Seeds are the index, except
+# for 6: workload 3 (same seed, lengths and page table) with an fp8 cache.
 WORKLOADS = {
     1: Workload("tiny", 2, 1, 16, "bf16", 1.0, False, seqlens=(64, 100), seed=1,
                 description="B2 s_q1 h_q16 bf16, s_k {64,100}, non-causal"),
@@ -74,6 +84,9 @@ WORKLOADS = {
     5: Workload("longctx_bs4_hq128", 4, 1, 128, "bf16", 1.0, False,
                 seqlens=(65536, 98304, 131072, 131072), seed=5,
                 description="B4 s_q1 h_q128 bf16, s_k {64K,96K,128K,128K}"),
+    6: Workload("varlen_bs128_hq16_fp8kv", 128, 1, 16, "bf16", 1.0, False, seqlen_range=(1, 8192), seed=3,
+                kv="fp8",
+                description="B128 s_q1 h_q16 bf16 q, fp8 e4m3 KV with per-page scales, s_k ~ U[1,8192]"),
 }
 
 
@@ -86,11 +99,13 @@ class DecodeInputs:
     softmax_scale: float
     causal: bool
     dtype: str
+    k_scale: Optional[torch.Tensor] = None       # fp8 cache: [num_pages] fp32
 
     def to(self, device) -> "DecodeInputs":
         return DecodeInputs(self.q.to(device), self.k_cache.to(device),
                             self.block_table.to(device), self.cache_seqlens.to(device),
-                            self.softmax_scale, self.causal, self.dtype)
+                            self.softmax_scale, self.causal, self.dtype,
+                            None if self.k_scale is None else self.k_scale.to(device))
 
 
 def pages_of(n: int) -> int:
@@ -102,10 +117,17 @@ def make_inputs(batch: int, s_q: int, h_q: int, dtype: str = "bf16", *,
                 seqlen_range: Optional[tuple] = None,
                 sigma: float = 1.0, causal: bool = False, seed: int = 0,
                 extra_pages: int = 0, poison: bool = False,
-                max_pages: Optional[int] = None) -> DecodeInputs:
+                max_pages: Optional[int] = None, kv_dtype: str = "same",
+                scale_mode: str = "amax") -> DecodeInputs:
     """Draw one seeded workload following the recipe in the module docstring."""
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+    if kv_dtype not in ("same", "fp8"):
+        raise ValueError("kv_dtype must be 'same' or 'fp8'")
+    if kv_dtype == "fp8" and dtype != "bf16":
+        raise ValueError("an fp8 cache goes with a bf16 q")
+    if scale_mode not in ("amax", "pow2", "none"):
+        raise ValueError("scale_mode must be 'amax', 'pow2' or 'none'")
     g = torch.Generator("cpu").manual_seed(int(seed))
     if seqlens is not None:
         sl = torch.tensor([int(x) for x in seqlens], dtype=torch.int64)
@@ -132,12 +154,31 @@ def make_inputs(batch: int, s_q: int, h_q: int, dtype: str = "bf16", *,
         pos += p
     tdt = _DTYPES[dtype]
     q = (torch.randn(batch, s_q, h_q, D_K, generator=g) * sigma).to(tdt)
-    k = (torch.randn(max(total, 1), PAGE, 1, D_K, generator=g) * sigma).to(tdt)
-    if poison:
-        _poison(q, k, bt, sl, perm[used:] if total > used else None)
+    k = torch.randn(max(total, 1), PAGE, 1, D_K, generator=g) * sigma
+    k_scale = None
+    if kv_dtype == "fp8":
+        if poison:
+            _poison(q, k, bt, sl, perm[used:] if total > used else None)
+        k, k_scale = _encode_fp8(k, scale_mode)
+    else:
+        k = k.to(tdt)
+        if poison:
+            _poison(q, k, bt, sl, perm[used:] if total > used else None)
     return DecodeInputs(q=q, k_cache=k, block_table=bt,
                         cache_seqlens=sl.to(torch.int32),
-                        softmax_scale=1.0 / (D_K ** 0.5), causal=causal, dtype=dtype)
+                        softmax_scale=1.0 / (D_K ** 0.5), causal=causal, dtype=dtype, k_scale=k_scale)
+
+
+def _encode_fp8(k: torch.Tensor, scale_mode: str):
+    """fp32 cache -> (e4m3fn codes, per-page fp32 scales or None)."""
+    if scale_mode == "none":
+        return k.clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn), None
+    amax = k.abs().amax(dim=(1, 2, 3)).clamp_min(1e-30)
+    scale = amax / FP8_MAX
+    if scale_mode == "pow2":
+        scale = torch.exp2(torch.ceil(torch.log2(scale)))
+    codes = (k / scale.view(-1, 1, 1, 1)).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes, scale.to(torch.float32).contiguous()
 
 
 def _poison(q, k, bt, sl, unused_pages):
@@ -155,10 +196,10 @@ def _poison(q, k, bt, sl, unused_pages):
 
 
 def workload_inputs(index: int, poison: bool = False, **overrides) -> DecodeInputs:
-    """Inputs of one of the five named workloads (seed = index)."""
+    """Inputs of one of the named workloads."""
     w = WORKLOADS[int(index)]
     kw = dict(seqlens=w.seqlens, seqlen_range=w.seqlen_range, sigma=w.sigma,
-              causal=w.causal, seed=w.seed, poison=poison)
+              causal=w.causal, seed=w.seed, poison=poison, kv_dtype=w.kv)
     kw.update(overrides)
     return make_inputs(w.batch, w.s_q, w.h_q, w.dtype, **kw)
 

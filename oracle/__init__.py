@@ -13,6 +13,7 @@ decode    exact attention over the paged latent KV cache, fp64 (NumPy), plus a
           pure-Python brute force for tiny shapes and a merge-by-LSE of partial
           results.
 metadata  integer re-derivation of the split-KV tile schedule.
+fp8       exact values of an fp8 e4m3 latent cache with per-page scales.
 """
 
 from .decode import (  # noqa: F401
@@ -27,3 +28,4 @@ from .decode import (  # noqa: F401
     PAGE,
 )
 from .metadata import oracle_metadata, schedule_chunks  # noqa: F401
+from .fp8 import decode_e4m3fn, dequantize_cache, e4m3fn_value  # noqa: F401

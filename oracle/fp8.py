@@ -1,0 +1,90 @@
+"""fp8 e4m3 codes of a latent KV cache -> exact values (fp64 CPU oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Sources (page title, then section):
+  [RUIBAO-FP8]   "DeepSeek开源FlashMLA全解析：性能革命背后的技术密码", section
+                 "1.2 计算模式创新：混合精度矩阵乘法": the query-key product is
+                 formed from fp8 values while the softmax and the value product
+                 stay in 16-bit floats.
+  [LITE-FP8]     "云上AI推理新突破：FlashMLA赋能DeepSeek-V2-Lite提速16%", section
+                 "3. 动态精度缩放": the same split, with fp8 casts of q and k.
+
+Reading (listed in the design notes): the pages name fp8 for the key side but
+fix neither the encoding nor a scale.  Here the cached latent rows are stored
+as fp8 codes in the OCP e4m3 "fn" encoding (1 sign bit, 4 exponent bits with
+bias 7, 3 mantissa bits; exponent field 0 is subnormal; no infinities; the two
+codes with every exponent and mantissa bit set are NaN) with one fp32 scale
+per 64-token page: the cached value is code value * scale[page].  q stays bf16
+and the attention is the one of decode.py over those values.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+EXP_BIAS = 7
+MAN_BITS = 3
+
+
+def e4m3fn_value(code: int) -> float:
+    """Value of one e4m3fn byte, from the bit fields (pure Python)."""
+    code = int(code)
+    if not 0 <= code <= 255:
+        raise ValueError("an fp8 code is one byte")
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> MAN_BITS) & 0xF
+    m = code & ((1 << MAN_BITS) - 1)
+    if e == 0xF and m == (1 << MAN_BITS) - 1:
+        return math.nan
+    if e == 0:                                  # subnormal: m/8 * 2^(1-bias)
+        return sign * math.ldexp(m, 1 - EXP_BIAS - MAN_BITS)
+    return sign * math.ldexp((1 << MAN_BITS) + m, e - EXP_BIAS - MAN_BITS)
+
+
+def _table() -> np.ndarray:
+    return np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+_VALUES = _table()
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """Array of e4m3fn codes (uint8, or a torch float8_e4m3fn / uint8 tensor)
+    -> float64 values of the same shape."""
+    try:
+        import torch
+
+        if isinstance(codes, torch.Tensor):
+            if codes.dtype != torch.uint8:
+                codes = codes.view(torch.uint8)
+            codes = codes.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    codes = np.asarray(codes)
+    if codes.dtype != np.uint8:
+        raise ValueError("codes must be uint8")
+    return _VALUES[codes]
+
+
+def dequantize_cache(codes, k_scale=None) -> np.ndarray:
+    """fp8 cache [num_pages, 64, h_kv, 576] of codes and its per-page scales
+    [num_pages] (None: every scale is 1) -> float64 cache of the same shape
+    holding code value * scale[page]."""
+    v = decode_e4m3fn(codes)
+    if k_scale is None:
+        return v
+    try:
+        import torch
+
+        if isinstance(k_scale, torch.Tensor):
+            k_scale = k_scale.detach().cpu().to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    s = np.asarray(k_scale, dtype=np.float64)
+    if s.shape != (v.shape[0],):
+        raise ValueError("k_scale must hold one scale per page")
+    return v * s.reshape((-1,) + (1,) * (v.ndim - 1))

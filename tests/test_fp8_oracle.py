@@ -1,0 +1,133 @@
+"""Pins for the fp8 side of the oracle (no GPU).
+
+The e4m3fn decoder is checked against torch's own float8_e4m3fn type (an
+independent implementation of the same OCP encoding) on all 256 codes, against
+values derived by hand from the bit fields, and against the ordering and sign
+symmetry the encoding implies.  The per-page scale is pinned with pages whose
+codes are all one value, so a scale applied along the wrong axis fails.  The
+fp8 input generator is checked to stay within e4m3's rounding error of the
+same draw in bf16.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute_force_decode, decode_e4m3fn, dequantize_cache, e4m3fn_value, oracle_decode
+from mla_decode_attention_02_amd.workloads import make_inputs
+
+
+def test_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    # -0.0 keeps its sign
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+# (code, value) from the bit fields: sign | eeee | mmm, bias 7, subnormal at e = 0
+HAND = [
+    (0x00, 0.0),
+    (0x01, 2.0 ** -9),            # smallest subnormal: 1/8 * 2^-6
+    (0x07, 7 * 2.0 ** -9),        # largest subnormal: 7/8 * 2^-6
+    (0x08, 2.0 ** -6),            # smallest normal
+    (0x38, 1.0),                  # e = 7
+    (0x3C, 1.5),                  # e = 7, m = 4
+    (0x40, 2.0),
+    (0x77, 240.0),                # 1.875 * 2^7
+    (0x78, 256.0),                # e = 15, m = 0 is an ordinary value (no infinities)
+    (0x7E, 448.0),                # largest finite: 1.75 * 2^8
+    (0xC0, -2.0),
+    (0xB8, -1.0),
+    (0xFE, -448.0),
+]
+
+
+@pytest.mark.parametrize("code,value", HAND, ids=[f"0x{c:02X}" for c, _ in HAND])
+def test_hand_values(code, value):
+    assert e4m3fn_value(code) == value
+    assert decode_e4m3fn(np.array([code], dtype=np.uint8))[0] == value
+
+
+def test_nan_codes():
+    assert math.isnan(e4m3fn_value(0x7F)) and math.isnan(e4m3fn_value(0xFF))
+    v = decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    assert int(np.isnan(v).sum()) == 2
+
+
+def test_order_and_sign_symmetry():
+    v = decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0), "codes 0x00..0x7E must increase strictly"
+    for c in range(0x7F):
+        assert v[c | 0x80] == -v[c]
+    # spacing: 8 values per binade above the subnormals, step 2^(e-10)
+    for e in range(1, 15):
+        step = np.diff(v[e * 8:(e + 1) * 8 + 1])
+        assert np.all(step == 2.0 ** (e - 10))
+
+
+def test_dequantize_applies_one_scale_per_page():
+    n_pages = 5
+    codes = np.full((n_pages, 64, 1, 576), 0x38, dtype=np.uint8)   # every value 1.0
+    codes[2, 10, 0, 3] = 0x40                                       # one 2.0 on page 2
+    scale = np.array([0.5, 3.0, 0.125, 7.25, 1e-3], dtype=np.float32)
+    k = dequantize_cache(codes, scale)
+    for p in range(n_pages):
+        expect = np.full((64, 1, 576), float(scale[p]))
+        if p == 2:
+            expect[10, 0, 3] = 2.0 * float(scale[p])
+        assert np.array_equal(k[p], expect)
+    assert np.array_equal(dequantize_cache(codes, None), decode_e4m3fn(codes))
+    with pytest.raises(ValueError):
+        dequantize_cache(codes, scale[:4])
+
+
+def test_accepts_torch_fp8_tensors():
+    t = torch.tensor([1.0, -2.0, 448.0, 0.0], dtype=torch.float32).to(torch.float8_e4m3fn)
+    assert decode_e4m3fn(t).tolist() == [1.0, -2.0, 448.0, 0.0]
+
+
+@pytest.mark.parametrize("mode", ["amax", "pow2", "none"])
+def test_generator_stays_within_e4m3_rounding(mode):
+    seqlens = (200, 64, 1)
+    x8 = make_inputs(3, 1, 4, "bf16", seqlens=seqlens, seed=12, extra_pages=1, kv_dtype="fp8",
+                     scale_mode=mode)
+    xb = make_inputs(3, 1, 4, "bf16", seqlens=seqlens, seed=12, extra_pages=1)
+    assert x8.k_cache.dtype == torch.float8_e4m3fn
+    assert torch.equal(x8.q, xb.q) and torch.equal(x8.block_table, xb.block_table)
+    k = dequantize_cache(x8.k_cache, x8.k_scale)
+    kb = xb.k_cache.double().numpy()          # the same draw, rounded to bf16
+    if mode == "none":
+        assert x8.k_scale is None
+        s = np.ones(k.shape[0])
+    else:
+        s = x8.k_scale.double().numpy()
+        assert x8.k_scale.dtype == torch.float32 and s.shape == (k.shape[0],)
+        if mode == "pow2":
+            assert np.all(np.frexp(s)[0] == 0.5), "pow2 scales must be powers of two"
+        else:
+            # the page maximum maps to the largest code
+            amax = np.abs(k).reshape(k.shape[0], -1).max(axis=1)
+            assert np.allclose(amax, 448.0 * s, rtol=0, atol=0)
+    bound = (2.0 ** -4 + 2.0 ** -8) * np.abs(kb) + s.reshape(-1, 1, 1, 1) * 2.0 ** -9
+    assert np.all(np.abs(k - kb) <= bound)
+
+
+def test_fp8_cache_brute_force():
+    x = make_inputs(2, 2, 3, "bf16", seqlens=(70, 5), seed=4, causal=True, kv_dtype="fp8")
+    k = dequantize_cache(x.k_cache, x.k_scale)
+    out, lse = oracle_decode(x.q, k, x.block_table, x.cache_seqlens, x.softmax_scale, True)
+    bo, bl = brute_force_decode(x.q, k, x.block_table, x.cache_seqlens, x.softmax_scale, True)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_generator_rejects_fp8_with_fp16():
+    with pytest.raises(ValueError):
+        make_inputs(1, 1, 1, "fp16", seqlens=(3,), kv_dtype="fp8")
