@@ -110,7 +110,8 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
     if seqlens is None:
         from mla_decode_attention_02_amd.workloads import workload_seqlens
         seqlens = workload_seqlens(workload)
-    flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q)
+    flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q,
+                                                     kv_elem=1 if w.kv == "fp8" else 2)
     alg = kv + qb + tb
     rec = {"kernel": kernel, "workload": w.name, "source_hash": kernel_source_hash(kernel),
            "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
@@ -153,13 +154,16 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
     return path
 
 
-def algorithmic_counts(seqlens, batch, s_q, h_q, elem=2):
+def algorithmic_counts(seqlens, batch, s_q, h_q, elem=2, kv_elem=2):
     """FLOPs and bytes of one decode step, counted from the definition:
     FLOPs = sum_b 2*h_q*s_q*s_k,b*(576+512); bytes = KV rows once (V lies inside
-    K) + Q + O + LSE + the block-table entries and lengths that are read."""
+    K; kv_elem bytes per element, plus a 4-byte scale per page for an fp8
+    cache) + Q + O + LSE + the block-table entries and lengths that are read."""
     rows = s_q * h_q
     flops = sum(2.0 * rows * n * (D_K + D_V) for n in seqlens)
-    kv = sum(n * D_K * elem for n in seqlens)
+    kv = sum(n * D_K * kv_elem for n in seqlens)
+    if kv_elem == 1:
+        kv += sum((n + PAGE - 1) // PAGE for n in seqlens) * 4
     q = batch * rows * D_K * elem
     o = batch * rows * D_V * elem
     lse = batch * rows * 4
@@ -180,7 +184,12 @@ def cpu_baseline(inputs, seconds: float):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     qf = inputs.q.double().numpy()
-    kf = inputs.k_cache.double().numpy()
+    if inputs.k_scale is not None or str(inputs.k_cache.dtype) == "torch.float8_e4m3fn":
+        from oracle import dequantize_cache
+
+        kf = dequantize_cache(inputs.k_cache, inputs.k_scale)
+    else:
+        kf = inputs.k_cache.double().numpy()
     B, s_q, h_q, _ = qf.shape
     seq = inputs.cache_seqlens.tolist()
     done, flops, results = 0, 0.0, {}
@@ -210,7 +219,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, help="1..5; 2 is the headline workload")
+    ap.add_argument("--workload", type=int, default=2, help="1..6; 2 is the headline workload, 6 is 3 with an fp8 cache")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -248,7 +257,8 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     host = workload_inputs(args.workload)
     seqlens = host.cache_seqlens.tolist()
-    flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q)
+    flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q,
+                                                     kv_elem=1 if w.kv == "fp8" else 2)
     step_bytes = kv + qb + ob + lseb + tb
     splitkv_bytes = kv + qb + tb   # what every split-KV launch must read
 
@@ -265,10 +275,12 @@ def main() -> int:
         k = caches[i % len(caches)]
         if ev is not None:
             ev[0].record()
-        api.mla_decode_splitkv(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+        api.mla_decode_splitkv(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
+                               g.k_scale)
         if ev is not None:
             ev[1].record()
-        api.mla_decode_combine(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+        api.mla_decode_combine(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
+                               g.k_scale)
 
     for i in range(args.warmup):
         step(i)
@@ -328,7 +340,8 @@ def main() -> int:
         "data": "synthetic: seeded randn q/KV, shuffled 64-token page table",
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
                    "s_k": "4096" if args.workload == 2 else w.description, "d_k": D_K, "d_v": D_V,
-                   "page": PAGE, "causal": w.causal, "num_parts": num_parts, "kv_copies": len(caches)},
+                   "page": PAGE, "causal": w.causal, "num_parts": num_parts, "kv_copies": len(caches),
+                   "kv_cache": "fp8_e4m3 + per-page fp32 scale" if w.kv == "fp8" else w.dtype},
         "effective_hbm_gbps": round(gbps, 1),
         "effective_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),

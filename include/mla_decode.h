@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 #define MLA_D_K 576             /* cached row width = query width           */
 #define MLA_D_V 512             /* value width: the first 512 columns       */
@@ -76,6 +76,18 @@ typedef enum {
 } mla_status;
 
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
+
+/* Element type of k_cache: the dtype of q (default), or fp8 e4m3 codes (OCP
+ * "e4m3fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, codes 0x7F/0xFF are NaN) times a per-page fp32 scale.
+ * Pages "DeepSeek开源FlashMLA全解析：性能革命背后的技术密码" (section "1.2
+ * 计算模式创新：混合精度矩阵乘法") and "云上AI推理新突破：FlashMLA赋能
+ * DeepSeek-V2-Lite提速16%" (section "3. 动态精度缩放") form the Q.K^T product
+ * from fp8 casts of q and k and keep the softmax and the value product in 16
+ * bits; here the latent cache itself is stored in fp8, converted exactly to
+ * bf16 on chip, and the page scale is applied to the scores and to the
+ * probabilities, which halves the bytes a memory-bound decode reads. */
+typedef enum { MLA_KV_SAME = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype;
 
 /* Text of the last error raised on the calling thread ("" if none); never NULL.
  * The pointer stays valid until the next call into the library on this thread. */
@@ -165,11 +177,16 @@ typedef struct {
   void* out;                   /* device [batch, s_q, h_q, 512], dtype        */
   int64_t out_stride[3];       /*   strides of batch, token, head             */
   float* lse;                  /* device [batch, s_q, h_q] fp32, contiguous   */
+  int kv_dtype;                /* mla_kv_dtype of k_cache (k_stride counts its elements) */
+  const float* k_scale;        /* MLA_KV_FP8_E4M3: device [num_pages] fp32, finite
+                                  (K = code value * k_scale[page]); NULL means 1 */
 } mla_decode_args;
 
 /*
  * Paged MLA decode: mla_decode_splitkv followed by mla_decode_combine on
  * `stream`.  Writes out and lse for every (b, i, h).
+ * An fp8 cache (kv_dtype = MLA_KV_FP8_E4M3) needs dtype bf16 and s_q*h_q <= 16
+ * (UNSUPPORTED otherwise); k_cache is then 8-byte aligned instead of 16.
  * Alignment: q, k_cache, out must be 16-byte aligned, as must every stride
  * times the element size (q_stride[*], k_stride[0..1], out_stride[*] multiples
  * of 8); lse and the int32 arrays 4-byte aligned.

@@ -68,6 +68,7 @@ class DecodeArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64 * 3),
         ("lse", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int), ("k_scale", ctypes.c_void_p),
     ]
 
 
@@ -157,7 +158,7 @@ def workspace_size(batch: int, s_q: int, h_q: int, num_parts: int) -> int:
 
 
 def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
-                workspace, out, lse) -> DecodeArgs:
+                workspace, out, lse, k_scale=None) -> DecodeArgs:
     a = DecodeArgs()
     a.dtype = DTYPE_CODES[q.dtype]
     a.batch, a.s_q, a.h_q = q.shape[0], q.shape[1], q.shape[2]
@@ -182,14 +183,22 @@ def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, s
     a.out = out.data_ptr()
     a.out_stride[:] = list(out.stride()[:3])
     a.lse = lse.data_ptr()
+    a.kv_dtype = 1 if k_cache.dtype == torch.float8_e4m3fn else 0
+    a.k_scale = k_scale.data_ptr() if k_scale is not None else None
     return a
 
 
-def _validate_tensors(q, k_cache, block_table, cache_seqlens):
+def _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale=None):
     if q.dtype not in DTYPE_CODES:
         raise ValueError("q must be bf16 or fp16")
-    if k_cache.dtype != q.dtype:
-        raise ValueError("k_cache dtype must match q")
+    if k_cache.dtype != q.dtype and not (k_cache.dtype == torch.float8_e4m3fn and q.dtype == torch.bfloat16):
+        raise ValueError("k_cache dtype must match q, or be float8_e4m3fn with a bf16 q")
+    if k_scale is not None:
+        if k_cache.dtype != torch.float8_e4m3fn:
+            raise ValueError("k_scale applies to an fp8 cache only")
+        if k_scale.dtype != torch.float32 or k_scale.dim() != 1 or k_scale.shape[0] != k_cache.shape[0] \
+                or not k_scale.is_contiguous() or k_scale.device != q.device:
+            raise ValueError("k_scale must be a contiguous fp32 [num_pages] tensor on q's device")
     if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2 or cache_seqlens.dim() != 1:
         raise ValueError("expected q [B,s_q,h_q,576], k_cache [pages,64,1,576], block_table [B,P], cache_seqlens [B]")
     if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
@@ -214,15 +223,16 @@ class DecodeBuffers:
         self.workspace = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
 
 
-def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
-    _validate_tensors(q, k_cache, block_table, cache_seqlens)
+def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+          k_scale=None):
+    _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale)
     if metadata is None:
         metadata = get_metadata(cache_seqlens, q.shape[1], q.shape[2], k_cache.shape[2])
     sched, offs = metadata
     if buffers is None:
         buffers = DecodeBuffers(q, sched.shape[0])
     a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
-                    buffers.workspace, buffers.out, buffers.lse)
+                    buffers.workspace, buffers.out, buffers.lse, k_scale)
     _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
     return buffers.out, buffers.lse
 
@@ -230,35 +240,42 @@ def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal
 def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
                cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
                metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-               buffers: Optional[DecodeBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+               buffers: Optional[DecodeBuffers] = None,
+               k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MLA decode.  Returns (out [B, s_q, h_q, 512] in q's dtype,
     lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result
-    (computed here when omitted); `buffers` lets a caller reuse outputs."""
-    return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers)
+    (computed here when omitted); `buffers` lets a caller reuse outputs.  An
+    fp8 cache (torch.float8_e4m3fn, with a bf16 q and s_q*h_q <= 16) takes an
+    optional per-page power-of-two `k_scale` [num_pages] fp32."""
+    return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+                 k_scale)
 
 
 def mla_decode_fused(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
                      cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
                      metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-                     buffers: Optional[DecodeBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     buffers: Optional[DecodeBuffers] = None,
+                     k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MLA decode with the merge of split requests (up to 4 pieces) done
     inside the split-KV kernel; same result as mla_decode.  `buffers` must come
     from DecodeBuffers (zero-filled workspace) and not be shared by two calls
     in flight on different streams."""
     return _call("mla_decode_fused", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata,
-                 buffers)
+                 buffers, k_scale)
 
 
-def mla_decode_splitkv(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+def mla_decode_splitkv(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+                       k_scale=None):
     """First phase only (the split-KV kernel)."""
     return _call("mla_decode_splitkv", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
-                 metadata, buffers)
+                 metadata, buffers, k_scale)
 
 
-def mla_decode_combine(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+def mla_decode_combine(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+                       k_scale=None):
     """Second phase only (merge of split pieces)."""
     return _call("mla_decode_combine", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
-                 metadata, buffers)
+                 metadata, buffers, k_scale)
 
 
 def mla_merge_partials(part_out: torch.Tensor, part_lse: torch.Tensor,

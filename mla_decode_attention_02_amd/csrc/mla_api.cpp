@@ -80,13 +80,20 @@ mla_status check_decode(const mla_decode_args* a) {
     return fail(MLA_ERROR_UNSUPPORTED, "page_size must be 64 (got %d)", a->page_size);
   mla_status st = check_shape(a->batch, a->s_q, a->h_q, a->h_kv);
   if (st != MLA_SUCCESS) return st;
+  if (a->kv_dtype != MLA_KV_SAME && a->kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERROR_UNSUPPORTED, "kv_dtype %d is not MLA_KV_SAME (0) or MLA_KV_FP8_E4M3 (1)", a->kv_dtype);
+  if (a->kv_dtype == MLA_KV_FP8_E4M3 && (a->dtype != MLA_DTYPE_BF16 || (long long)a->s_q * a->h_q > 16))
+    return fail(MLA_ERROR_UNSUPPORTED, "an fp8 cache needs dtype bf16 and s_q*h_q <= 16");
+  if (a->k_scale && !aligned(a->k_scale, 4)) return fail(MLA_ERROR_INVALID_VALUE, "k_scale must be 4-byte aligned");
   if (a->num_pages <= 0 || a->max_pages_per_seq <= 0 || a->num_parts <= 0)
     return fail(MLA_ERROR_INVALID_VALUE, "num_pages, max_pages_per_seq and num_parts must be positive");
   if (!a->q || !a->k_cache || !a->block_table || !a->cache_seqlens || !a->sched || !a->split_offsets ||
       !a->workspace || !a->out || !a->lse)
     return fail(MLA_ERROR_INVALID_VALUE, "a required pointer is NULL");
-  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->out, 16) || !aligned(a->workspace, 16))
-    return fail(MLA_ERROR_INVALID_VALUE, "q, k_cache, out and workspace must be 16-byte aligned");
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->workspace, 16))
+    return fail(MLA_ERROR_INVALID_VALUE, "q, out and workspace must be 16-byte aligned");
+  if (!aligned(a->k_cache, a->kv_dtype == MLA_KV_FP8_E4M3 ? 8 : 16))
+    return fail(MLA_ERROR_INVALID_VALUE, "k_cache must be 16-byte aligned (8 for an fp8 cache)");
   if (!aligned(a->lse, 4) || !aligned(a->block_table, 4) || !aligned(a->cache_seqlens, 4) ||
       !aligned(a->sched, 4) || !aligned(a->split_offsets, 4))
     return fail(MLA_ERROR_INVALID_VALUE, "lse and the int32 arrays must be 4-byte aligned");
@@ -123,6 +130,8 @@ mla::DecodeParams make_params(const mla_decode_args* a) {
   p.q_s0 = a->q_stride[0]; p.q_s1 = a->q_stride[1]; p.q_s2 = a->q_stride[2];
   p.k = a->k_cache;
   p.k_s0 = a->k_stride[0]; p.k_s1 = a->k_stride[1];
+  p.kv_fp8 = a->kv_dtype == MLA_KV_FP8_E4M3;
+  p.k_scale = a->k_scale;
   p.block_table = a->block_table;
   p.bt_s = a->bt_stride;
   p.seqlens = a->cache_seqlens;

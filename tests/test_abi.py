@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.mla_abi_version() == 2
+    assert L.mla_abi_version() == 3
     assert L.mla_last_error() is not None
 
 
@@ -146,6 +146,12 @@ BREAKS = [
     ("scale neg", lambda a: setattr(a, "softmax_scale", -0.5), INVALID),
     ("causal", lambda a: setattr(a, "causal", 2), INVALID),
     ("workspace small", lambda a: setattr(a, "workspace_bytes", 1024), WS_SMALL),
+    ("kv_dtype", lambda a: setattr(a, "kv_dtype", 2), UNSUPPORTED),
+    ("fp8 with fp16 q", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "dtype", 1)), UNSUPPORTED),
+    ("fp8 with 32 rows", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "h_q", 32)), UNSUPPORTED),
+    ("fp8 k misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "k_cache", (1 << 21) + 4)), INVALID),
+    ("k_scale misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "k_scale", 10 * (1 << 20) + 2)),
+     INVALID),
 ]
 
 

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import oracle_decode, oracle_decode_rows, oracle_metadata
+from oracle import dequantize_cache, oracle_decode, oracle_decode_rows, oracle_metadata
 from mla_decode_attention_02_amd import api
 from mla_decode_attention_02_amd.workloads import WORKLOADS, make_inputs, workload_inputs, workload_seqlens
 
@@ -45,18 +45,26 @@ def run(x, num_parts=None, entry="mla_decode", buffers=None):
     g = x.to(dev)
     meta = api.get_metadata(g.cache_seqlens, g.q.shape[1], g.q.shape[2], num_parts=num_parts)
     out, lse = getattr(api, entry)(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale,
-                                   g.causal, metadata=meta, buffers=buffers)
+                                   g.causal, metadata=meta, buffers=buffers, k_scale=g.k_scale)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), [m.cpu().numpy() for m in meta]
 
 
-def compare(out, lse, ref_o, ref_l, tag):
+def kv64(x):
+    """The cache as the oracle sees it: exact values in float64 (an fp8 cache
+    through the oracle's own e4m3 decoder and page scales)."""
+    if x.k_cache.dtype == torch.float8_e4m3fn:
+        return dequantize_cache(x.k_cache, x.k_scale)
+    return x.k_cache.double().numpy()
+
+
+def compare(out, lse, ref_o, ref_l, tag, tol_o=TOL_O):
     fin = np.isfinite(ref_l)
     assert np.array_equal(fin, np.isfinite(lse)), f"{tag}: -inf pattern differs"
     assert not np.isnan(out).any(), f"{tag}: NaN in output"
     do = np.abs(out - ref_o).max() if out.size else 0.0
     dl = np.abs(lse[fin] - ref_l[fin]).max() if fin.any() else 0.0
-    assert do <= TOL_O, f"{tag}: max|dO| = {do}"
+    assert do <= tol_o, f"{tag}: max|dO| = {do}"
     assert dl <= TOL_LSE, f"{tag}: max|dLSE| = {dl}"
     if not fin.all():
         assert np.all(out[~fin] == 0), f"{tag}: rows with no visible key must be 0"
@@ -85,7 +93,7 @@ def test_metadata_bit_exact(seqlens, parts):
     assert np.array_equal(offs.cpu().numpy(), ref_o)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_metadata_workloads_bit_exact(idx):
     w = WORKLOADS[idx]
     seqlens = workload_seqlens(idx)
@@ -172,6 +180,66 @@ def test_strided_views():
     assert not obig[..., 512:].any(), "padding of the output rows was written"
 
 
+# ------------------------------------------------------------ fp8 cache --
+FP8_EDGE = [
+    # (s_q, h_q, seqlens, causal, scale_mode, num_parts)
+    (1, 16, (1, 2, 63, 64, 65), False, "amax", None),
+    (1, 16, (127, 128, 129, 1000), False, "pow2", 3),
+    (2, 8, (1, 2, 63, 64, 65, 129), True, "amax", 2),
+    (1, 1, (5, 300), False, "none", 1),
+    (1, 3, (300, 7), False, "amax", 5),
+    (4, 4, (3, 200, 64), True, "pow2", 4),
+    (1, 16, (2000, 1, 700), False, "amax", 9),
+]
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("s_q,h_q,seqlens,causal,mode,parts", FP8_EDGE,
+                         ids=[f"sq{c[0]}_hq{c[1]}_{'c' if c[3] else 'n'}_{c[4]}_p{c[5]}" for c in FP8_EDGE])
+def test_fp8_small_parity(s_q, h_q, seqlens, causal, mode, parts, entry):
+    tag = f"fp8 {entry} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} scale={mode} parts={parts}"
+    _say(tag)
+    x = make_inputs(len(seqlens), s_q, h_q, "bf16", seqlens=seqlens, causal=causal, seed=sum(seqlens) + 7 * h_q,
+                    poison=True, extra_pages=2, kv_dtype="fp8", scale_mode=mode)
+    out, lse, _ = run(x, parts, entry)
+    ref_o, ref_l = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+    compare(out, lse, ref_o, ref_l, tag)
+
+
+def test_fp8_scale_is_applied_per_page():
+    """One used page's scale is tripled: the result must follow the oracle, which
+    a kernel that ignored the scale, or took another page's, would not (the
+    two oracle results differ by several units).  That page's values, and so
+    the outputs and their bf16 rounding step, grow up to threefold: the output
+    tolerance grows with them."""
+    _say("fp8 per-page scale")
+    x = make_inputs(2, 1, 16, "bf16", seqlens=(300, 129), seed=77, kv_dtype="fp8")
+    before, _ = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    x.k_scale[int(x.block_table[0, 2])] *= 3.0
+    out, lse, _ = run(x, 3)
+    ref_o, ref_l = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    assert np.abs(ref_o - before).max() > 1.0
+    compare(out, lse, ref_o, ref_l, "fp8 page scale x3", tol_o=3 * TOL_O)
+
+
+def test_fp8_unused_slots_and_pages_are_never_read_bitwise():
+    _say("fp8: garbage codes in unused slots, NaN codes in unused pages")
+    seqlens = (70, 130, 3)
+    x = make_inputs(3, 1, 16, "bf16", seqlens=seqlens, seed=29, extra_pages=4, kv_dtype="fp8")
+    out1, lse1, _ = run(x, 4)
+    raw = x.k_cache.view(torch.uint8)
+    for b, nlen in enumerate(seqlens):
+        p = (nlen + 63) // 64
+        raw[int(x.block_table[b, p - 1]), nlen % 64:, 0, :] = 0xFE      # -448, finite
+    used = set(int(v) for v in x.block_table.flatten().tolist() if v >= 0)
+    for page in range(x.k_cache.shape[0]):
+        if page not in used:
+            raw[page] = 0x7F                                            # NaN codes
+            x.k_scale[page] = float("nan")
+    out2, lse2, _ = run(x, 4)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
 # ------------------------------------------------------------ invariants --
 def test_page_permutation_is_bitwise_invariant():
     _say("page permutation invariance")
@@ -241,7 +309,7 @@ def test_fused_repeated_calls_reuse_counters(h_q):
 
 # ----------------------------------------------------- full-size samples --
 @pytest.mark.parametrize("entry", ENTRIES)
-@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6])
 def test_workload_full_size_sampled(idx, entry):
     """Full-size workload in the launch configuration the benchmark uses;
     the oracle checks a sample of requests (first, last, and the longest)."""
@@ -255,7 +323,7 @@ def test_workload_full_size_sampled(idx, entry):
     whole = [b for b in range(w.batch) if offs[b + 1] - offs[b] == 1]
     picks = sorted(set([0, w.batch - 1, int(np.argmax(seqlens))] + split[:1] + whole[:1]))
     qf = x.q.double().numpy()
-    kf = x.k_cache.double().numpy()
+    kf = kv64(x)
     for b in picks:
         ref_o, ref_l = oracle_decode_rows(qf, kf, x.block_table, x.cache_seqlens, x.softmax_scale,
                                           w.causal, b)
