@@ -204,9 +204,133 @@ def workload_inputs(index: int, poison: bool = False, **overrides) -> DecodeInpu
     return make_inputs(w.batch, w.s_q, w.h_q, w.dtype, **kw)
 
 
+# ------------------------------------------------------ general paged MHA --
+@dataclass
+class MhaInputs:
+    """Inputs of paged multi-head / grouped-query decode attention.
+
+      q            [B, s_q, h_q, d]             bf16/fp16
+      k_cache      [num_pages, 64, h_kv, d]     bf16/fp16
+      v_cache      [num_pages, 64, h_kv, d_v]   bf16/fp16
+      block_table  [B, max_pages]               int32 (-1 past a request's pages)
+      cache_seqlens[B]                          int32
+    """
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    cache_seqlens: torch.Tensor
+    softmax_scale: float
+    causal: bool
+    dtype: str
+
+    def to(self, device) -> "MhaInputs":
+        return MhaInputs(self.q.to(device), self.k_cache.to(device), self.v_cache.to(device),
+                         self.block_table.to(device), self.cache_seqlens.to(device),
+                         self.softmax_scale, self.causal, self.dtype)
+
+
+@dataclass(frozen=True)
+class MhaWorkload:
+    name: str
+    batch: int
+    s_q: int
+    h_q: int
+    h_kv: int
+    head_dim: int
+    dtype: str
+    causal: bool
+    seqlens: Optional[Sequence[int]] = None
+    seqlen_range: Optional[tuple] = None
+    seed: int = 0
+    description: str = field(default="", compare=False)
+
+
+# Grouped-query decode workloads (head size 128, the common LLM shape): one
+# GPU's share of a 64-query-head / 8-KV-head model, and a long-context batch.
+MHA_WORKLOADS = {
+    7: MhaWorkload("gqa_bs64_hq64_hkv8_d128", 64, 1, 64, 8, 128, "bf16", False, seqlen_range=(1, 8192), seed=7,
+                   description="B64 s_q1 h_q64 h_kv8 d128 bf16, s_k ~ U[1,8192]"),
+    8: MhaWorkload("gqa_longctx_bs8_hq32_hkv8_d128", 8, 1, 32, 8, 128, "bf16", False, seqlens=(32768,) * 8,
+                   seed=8, description="B8 s_q1 h_q32 h_kv8 d128 bf16, every s_k 32768"),
+}
+
+
+def make_mha_inputs(batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int, dtype: str = "bf16", *,
+                    head_dim_v: Optional[int] = None,
+                    seqlens: Optional[Sequence[int]] = None,
+                    seqlen_range: Optional[tuple] = None,
+                    sigma: float = 1.0, causal: bool = False, seed: int = 0,
+                    extra_pages: int = 0, poison: bool = False,
+                    max_pages: Optional[int] = None) -> MhaInputs:
+    """Seeded MHA/GQA decode inputs.  Same recipe as make_inputs, with the
+    draws in the order: lengths, page permutation, q [B,s_q,h_q,d],
+    k [N,64,h_kv,d], v [N,64,h_kv,d_v] (each torch.randn * sigma), then the cast
+    to the dtype.  Poison (correctness runs): slots past a request's length in
+    its last page and every unused page get K = +-POISON along the sign of the
+    first query row of the KV head's group and V = POISON."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+    if h_q % h_kv != 0:
+        raise ValueError("h_q must be a multiple of h_kv")
+    d_v = head_dim if head_dim_v is None else head_dim_v
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    if seqlens is not None:
+        sl = torch.tensor([int(x) for x in seqlens], dtype=torch.int64)
+        if sl.numel() != batch:
+            raise ValueError("len(seqlens) != batch")
+    elif seqlen_range is not None:
+        lo, hi = seqlen_range
+        sl = torch.randint(int(lo), int(hi) + 1, (batch,), generator=g, dtype=torch.int64)
+    else:
+        raise ValueError("give seqlens or seqlen_range")
+    n_pages = [pages_of(n) for n in sl.tolist()]
+    used = sum(n_pages)
+    total = used + int(extra_pages)
+    perm = torch.randperm(total, generator=g) if total > 0 else torch.zeros(0, dtype=torch.int64)
+    width = max(max(n_pages) if n_pages else 0, 1)
+    if max_pages is not None:
+        if max_pages < width:
+            raise ValueError("max_pages smaller than the longest request")
+        width = max_pages
+    bt = torch.full((batch, width), -1, dtype=torch.int32)
+    pos = 0
+    for b, p in enumerate(n_pages):
+        bt[b, :p] = perm[pos:pos + p].to(torch.int32)
+        pos += p
+    tdt = _DTYPES[dtype]
+    q = (torch.randn(batch, s_q, h_q, head_dim, generator=g) * sigma).to(tdt)
+    k = (torch.randn(max(total, 1), PAGE, h_kv, head_dim, generator=g) * sigma).to(tdt)
+    v = (torch.randn(max(total, 1), PAGE, h_kv, d_v, generator=g) * sigma).to(tdt)
+    if poison:
+        group = h_q // h_kv
+        for b in range(batch):
+            n = int(sl[b])
+            p = pages_of(n)
+            if p > 0 and n % PAGE != 0:
+                page = int(bt[b, p - 1])
+                for hk in range(h_kv):
+                    direction = torch.sign(q[b, 0, hk * group].float())
+                    direction[direction == 0] = 1.0
+                    k[page, n % PAGE:, hk, :] = (direction * POISON).to(tdt)
+                v[page, n % PAGE:] = POISON
+        if total > used:
+            k[perm[used:]] = POISON
+            v[perm[used:]] = POISON
+    return MhaInputs(q=q, k_cache=k, v_cache=v, block_table=bt, cache_seqlens=sl.to(torch.int32),
+                     softmax_scale=1.0 / (head_dim ** 0.5), causal=causal, dtype=dtype)
+
+
+def mha_workload_inputs(index: int, poison: bool = False, **overrides) -> MhaInputs:
+    w = MHA_WORKLOADS[int(index)]
+    kw = dict(seqlens=w.seqlens, seqlen_range=w.seqlen_range, causal=w.causal, seed=w.seed, poison=poison)
+    kw.update(overrides)
+    return make_mha_inputs(w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim, w.dtype, **kw)
+
+
 def workload_seqlens(index: int) -> List[int]:
     """Only the sequence lengths of a named workload (cheap: no tensors)."""
-    w = WORKLOADS[int(index)]
+    w = WORKLOADS[int(index)] if int(index) in WORKLOADS else MHA_WORKLOADS[int(index)]
     if w.seqlens is not None:
         return list(w.seqlens)
     g = torch.Generator("cpu").manual_seed(int(w.seed))

@@ -14,6 +14,8 @@ decode    exact attention over the paged latent KV cache, fp64 (NumPy), plus a
           results.
 metadata  integer re-derivation of the split-KV tile schedule.
 fp8       exact values of an fp8 e4m3 latent cache with per-page scales.
+mha       paged multi-head / grouped-query decode over separate K and V caches
+          (any head sizes, h_kv dividing h_q), fp64, with its split schedule.
 """
 
 from .decode import (  # noqa: F401
@@ -29,3 +31,4 @@ from .decode import (  # noqa: F401
 )
 from .metadata import oracle_metadata, schedule_chunks  # noqa: F401
 from .fp8 import decode_e4m3fn, dequantize_cache, e4m3fn_value  # noqa: F401
+from .mha import brute_force_mha, oracle_mha_decode, oracle_mha_metadata, oracle_mha_rows  # noqa: F401
