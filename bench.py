@@ -14,6 +14,9 @@ HIP events on the stream it runs on, and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+Workloads 7 and 8 time the paged grouped-query (MHA) path instead: schedule
+(mha_get_metadata), split-KV kernel and combine over separate K and V caches.
 """
 
 from __future__ import annotations
@@ -40,6 +43,7 @@ CSRC = os.path.join(ROOT, "mla_decode_attention_02_amd", "csrc")
 KERNEL_SOURCES = {
     "splitkv_wide_kernel": ["mla_splitkv_wide.hip", "mla_splitkv.hpp", "mla_common.hpp"],
     "splitkv_narrow_kernel": ["mla_splitkv_narrow.hip", "mla_splitkv.hpp", "mla_common.hpp"],
+    "mha_splitkv_kernel": ["mha_decode.hip", "mla_common.hpp"],
 }
 COPY_MIB = 1024
 
@@ -81,10 +85,11 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
     """Turn the rocprofv3 outputs of one workload (kernel trace, FETCH_SIZE and
     WRITE_SIZE passes, and the plain-copy calibration) into the summary kept
     under profiles/.  Runs on the host after the GPU run."""
-    from mla_decode_attention_02_amd.workloads import WORKLOADS
+    from mla_decode_attention_02_amd.workloads import MHA_WORKLOADS, WORKLOADS
 
-    w = WORKLOADS[workload]
-    kernel = "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
+    mha = workload in MHA_WORKLOADS
+    w = MHA_WORKLOADS[workload] if mha else WORKLOADS[workload]
+    kernel = "mha_splitkv_kernel" if mha else ("splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel")
     tag = f"w{workload}"
     stats = _counter_rows(os.path.join(out_dir, f"prof_{tag}", f"{tag}_kernel_stats.csv"))
 
@@ -110,8 +115,11 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
     if seqlens is None:
         from mla_decode_attention_02_amd.workloads import workload_seqlens
         seqlens = workload_seqlens(workload)
-    flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q,
-                                                     kv_elem=1 if w.kv == "fp8" else 2)
+    if mha:
+        flops, kv, qb, ob, lseb, tb = mha_algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim)
+    else:
+        flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q,
+                                                         kv_elem=1 if w.kv == "fp8" else 2)
     alg = kv + qb + tb
     rec = {"kernel": kernel, "workload": w.name, "source_hash": kernel_source_hash(kernel),
            "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
@@ -171,6 +179,114 @@ def algorithmic_counts(seqlens, batch, s_q, h_q, elem=2, kv_elem=2):
     return flops, kv, q, o, lse, tables
 
 
+def mha_algorithmic_counts(seqlens, batch, s_q, h_q, h_kv, d):
+    """FLOPs and bytes of one paged MHA/GQA decode step, from the definition:
+    FLOPs = sum_b 2*s_q*h_q*s_k,b*(d + d); bytes = K and V rows of every KV head
+    once (2*h_kv*d*2 per token) + Q + O + LSE + table entries and lengths."""
+    rows = s_q * h_q
+    flops = sum(2.0 * rows * n * (d + d) for n in seqlens)
+    kv = sum(n * h_kv * d * 2 * 2 for n in seqlens)
+    q = batch * rows * d * 2
+    o = batch * rows * d * 2
+    lse = batch * rows * 4
+    tables = sum((n + PAGE - 1) // PAGE for n in seqlens) * 4 + batch * 4
+    return flops, kv, q, o, lse, tables
+
+
+def bench_mha(args) -> dict:
+    """One step = mha_get_metadata + MHA split-KV + combine over a GQA workload."""
+    import torch
+
+    from mla_decode_attention_02_amd import api
+    from mla_decode_attention_02_amd.workloads import MHA_WORKLOADS, mha_workload_inputs
+
+    w = MHA_WORKLOADS[args.workload]
+    host = mha_workload_inputs(args.workload)
+    seqlens = host.cache_seqlens.tolist()
+    flops, kv, qb, ob, lseb, tb = mha_algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim)
+    step_bytes = kv + qb + ob + lseb + tb
+    splitkv_bytes = kv + qb + tb
+    g = host.to(torch.device("cuda:0"))
+    caches = [(g.k_cache, g.v_cache)] + [(g.k_cache.clone(), g.v_cache.clone())
+                                        for _ in range(max(1, args.copies) - 1)]
+    sched0, _ = api.mha_get_metadata(g.cache_seqlens, w.s_q, w.h_q, w.h_kv)
+    num_parts = sched0.shape[0]
+    bufs = api.MhaBuffers(g.q, w.h_kv, num_parts)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        meta = api.mha_get_metadata(g.cache_seqlens, w.s_q, w.h_q, w.h_kv, num_parts=num_parts)
+        k, v = caches[i % len(caches)]
+        if ev is not None:
+            ev[0].record()
+        api.mha_decode_splitkv(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+        if ev is not None:
+            ev[1].record()
+        api.mha_decode_combine(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = max(t0.elapsed_time(t1), wall * 1e3) / args.steps
+    ks = sorted(a.elapsed_time(b) for a, b in events)
+    kavg = sum(ks) / len(ks)
+    ach = splitkv_bytes / (kavg * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": stored_traffic("mha_splitkv_kernel", w.name),
+            "kernel": "mha_splitkv_kernel", "kernel_avg_us": round(kavg * 1e3, 2),
+            "kernel_p10_p90_us": [round(ks[len(ks) // 10] * 1e3, 2), round(ks[(9 * len(ks)) // 10] * 1e3, 2)],
+            "algorithmic_bytes_per_launch": splitkv_bytes, "algorithmic_flops_per_launch": flops}
+    result = {
+        "metric": "paged GQA decode effective HBM GB/s & roofline %",
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded randn q/K/V, shuffled 64-token page table",
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "head_dim": w.head_dim, "s_k": w.description, "page": PAGE, "causal": w.causal,
+                   "num_parts": num_parts, "kv_copies": len(caches)},
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle.mha import oracle_mha_rows
+
+        qf, kf, vf = host.q.double().numpy(), host.k_cache.double().numpy(), host.v_cache.double().numpy()
+        out = bufs.out.float().cpu().numpy()
+        lse = bufs.lse.cpu().numpy()
+        done, fl, dO, dL = 0, 0.0, 0.0, 0.0
+        t = time.perf_counter()
+        while time.perf_counter() - t < args.cpu_seconds or done == 0:
+            b = done % w.batch
+            o, l = oracle_mha_rows(qf, kf, vf, host.block_table, host.cache_seqlens, host.softmax_scale,
+                                   w.causal, b)
+            dO = max(dO, float(np.abs(out[b] - o).max()))
+            dL = max(dL, float(np.abs(lse[b] - l).max()))
+            fl += 2.0 * w.s_q * w.h_q * seqlens[b] * 2 * w.head_dim
+            done += 1
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s",
+                                  "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                  "sample": f"{done} whole requests of the same workload, fp64 NumPy, {dt:.1f} s"}
+        result["parity_vs_oracle"] = {"requests": done, "max_abs_dO": dO, "max_abs_dLSE": dL}
+    return result
+
+
 def cpu_baseline(inputs, seconds: float):
     """The oracle, as it stands, over whole requests of the same workload until
     `seconds` of CPU time have passed (at least one request)."""
@@ -219,7 +335,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, help="1..6; 2 is the headline workload, 6 is 3 with an fp8 cache")
+    ap.add_argument("--workload", type=int, default=2, help="1..8; 2 is the headline workload, 6 is 3 with an fp8 cache, 7-8 are GQA (MHA path)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,7 +367,11 @@ def main() -> int:
         return 0
 
     from mla_decode_attention_02_amd import api
-    from mla_decode_attention_02_amd.workloads import WORKLOADS, workload_inputs
+    from mla_decode_attention_02_amd.workloads import MHA_WORKLOADS, WORKLOADS, workload_inputs
+
+    if args.workload in MHA_WORKLOADS:
+        print(json.dumps(bench_mha(args)))
+        return 0
 
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]

@@ -1,4 +1,4 @@
-"""Thin torch binding of the C ABI in include/mla_decode.h.
+"""Thin torch binding of the C ABI in include/mla_decode.h and include/mha_decode.h.
 
 Argument marshalling only: every step of the decode path (scheduling, attention,
 combine) runs in the HIP kernels of libmla_decode.so.  torch provides device
@@ -72,6 +72,27 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class MhaArgs(ctypes.Structure):
+    """Mirror of mha_decode_args."""
+
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("batch", ctypes.c_int), ("s_q", ctypes.c_int), ("h_q", ctypes.c_int), ("h_kv", ctypes.c_int),
+        ("head_dim", ctypes.c_int), ("page_size", ctypes.c_int),
+        ("num_pages", ctypes.c_int), ("max_pages_per_seq", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("q_stride", ctypes.c_int64 * 3),
+        ("k_cache", ctypes.c_void_p), ("k_stride", ctypes.c_int64 * 3),
+        ("v_cache", ctypes.c_void_p), ("v_stride", ctypes.c_int64 * 3),
+        ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int64),
+        ("cache_seqlens", ctypes.c_void_p),
+        ("sched", ctypes.c_void_p), ("split_offsets", ctypes.c_void_p), ("num_parts", ctypes.c_int),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64 * 3),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
 def library_path() -> str:
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 
@@ -95,6 +116,16 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
         fn.argtypes = [ctypes.POINTER(DecodeArgs), p]
     L.mla_merge_partials.restype = st
     L.mla_merge_partials.argtypes = [ctypes.POINTER(MergeArgs), p]
+    L.mha_get_metadata_shape.restype = st
+    L.mha_get_metadata_shape.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.mha_get_metadata.restype = st
+    L.mha_get_metadata.argtypes = [p, i, i, i, p, p, p]
+    L.mha_workspace_size.restype = st
+    L.mha_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    for name in ("mha_decode", "mha_decode_splitkv", "mha_decode_combine"):
+        fn = getattr(L, name)
+        fn.restype = st
+        fn.argtypes = [ctypes.POINTER(MhaArgs), p]
     return L
 
 
@@ -312,3 +343,128 @@ def mla_merge_partials(part_out: torch.Tensor, part_lse: torch.Tensor,
     a.lse = lse.data_ptr()
     _check(lib().mla_merge_partials(ctypes.byref(a), _stream_ptr(part_out.device)))
     return out, lse
+
+
+# ----------------------------------------------------- paged MHA / GQA --
+def mha_get_metadata_shape(batch: int, s_q: int, h_q: int, h_kv: int, num_cus: int = 0) -> Tuple[int, int, int]:
+    """(num_parts, sched_elems, split_offsets_elems) of the MHA path."""
+    n, se, so = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().mha_get_metadata_shape(num_cus, batch, s_q, h_q, h_kv,
+                                        ctypes.byref(n), ctypes.byref(se), ctypes.byref(so)))
+    return n.value, se.value, so.value
+
+
+def mha_get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int,
+                     num_parts: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV schedule of the (request, KV head) units: (sched [num_parts, 8],
+    split_offsets [batch * h_kv + 1]), int32 on the device of cache_seqlens."""
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.dim() != 1:
+        raise ValueError("cache_seqlens must be a 1-D int32 device tensor")
+    seq = cache_seqlens.contiguous()
+    batch = seq.numel()
+    if num_parts is None:
+        with torch.cuda.device(seq.device):
+            num_parts, _, _ = mha_get_metadata_shape(batch, s_q, h_q, h_kv)
+    sched = torch.empty((num_parts, SCHED_FIELDS), dtype=torch.int32, device=seq.device)
+    offs = torch.empty((batch * h_kv + 1,), dtype=torch.int32, device=seq.device)
+    _check(lib().mha_get_metadata(seq.data_ptr(), batch, h_kv, num_parts, sched.data_ptr(), offs.data_ptr(),
+                                  _stream_ptr(seq.device)))
+    return sched, offs
+
+
+def mha_workspace_size(batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int, num_parts: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mha_workspace_size(batch, s_q, h_q, h_kv, head_dim, num_parts, ctypes.byref(n)))
+    return n.value
+
+
+class MhaBuffers:
+    """Outputs and workspace of one MHA decode shape, allocated once and reused."""
+
+    def __init__(self, q: torch.Tensor, h_kv: int, num_parts: int):
+        B, s_q, h_q, d = q.shape
+        self.out = torch.empty((B, s_q, h_q, d), dtype=q.dtype, device=q.device)
+        self.lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+        nbytes = mha_workspace_size(B, s_q, h_q, h_kv, d, num_parts)
+        self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+
+
+def _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens):
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError("q must be bf16 or fp16")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("k_cache and v_cache must have q's dtype")
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4 or block_table.dim() != 2 \
+            or cache_seqlens.dim() != 1:
+        raise ValueError("expected q [B,s_q,h_q,d], k_cache/v_cache [pages,64,h_kv,d], block_table [B,P], "
+                         "cache_seqlens [B]")
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[3] != q.shape[3]:
+        raise ValueError("k_cache and v_cache must both be [pages, 64, h_kv, d] with q's d")
+    if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
+        raise ValueError("block_table and cache_seqlens must be int32")
+    for t in (q, k_cache, v_cache, block_table, cache_seqlens):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    if q.stride(3) != 1 or k_cache.stride(3) != 1 or v_cache.stride(3) != 1 or block_table.stride(1) != 1:
+        raise ValueError("innermost dimensions must be contiguous")
+
+
+def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+    _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens)
+    B, s_q, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if metadata is None:
+        metadata = mha_get_metadata(cache_seqlens, s_q, h_q, h_kv)
+    sched, offs = metadata
+    if buffers is None:
+        buffers = MhaBuffers(q, h_kv, sched.shape[0])
+    a = MhaArgs()
+    a.dtype = DTYPE_CODES[q.dtype]
+    a.batch, a.s_q, a.h_q, a.h_kv = B, s_q, h_q, h_kv
+    a.head_dim, a.page_size = d, k_cache.shape[1]
+    a.num_pages, a.max_pages_per_seq = k_cache.shape[0], block_table.shape[1]
+    a.q = q.data_ptr()
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    for i in range(3):
+        a.q_stride[i] = q.stride(i)
+        a.k_stride[i] = k_cache.stride(i)
+        a.v_stride[i] = v_cache.stride(i)
+        a.out_stride[i] = buffers.out.stride(i)
+    a.block_table = block_table.data_ptr()
+    a.bt_stride = block_table.stride(0)
+    a.cache_seqlens = cache_seqlens.data_ptr()
+    a.sched, a.split_offsets, a.num_parts = sched.data_ptr(), offs.data_ptr(), sched.shape[0]
+    a.softmax_scale = float(softmax_scale)
+    a.causal = int(bool(causal))
+    a.workspace = buffers.workspace.data_ptr()
+    a.workspace_bytes = buffers.workspace.numel()
+    a.out = buffers.out.data_ptr()
+    a.lse = buffers.lse.data_ptr()
+    _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
+    return buffers.out, buffers.lse
+
+
+def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+               cache_seqlens: torch.Tensor, softmax_scale: Optional[float] = None, causal: bool = False,
+               metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+               buffers: Optional[MhaBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged MHA/GQA decode over separate K and V caches [pages, 64, h_kv, d]
+    (d in 64, 128, 256; query head h reads KV head h // (h_q // h_kv)).
+    Returns (out [B, s_q, h_q, d] in q's dtype, lse [B, s_q, h_q] fp32).
+    softmax_scale defaults to 1/sqrt(d)."""
+    if softmax_scale is None:
+        softmax_scale = q.shape[-1] ** -0.5
+    return _mha_call("mha_decode", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
+                     metadata, buffers)
+
+
+def mha_decode_splitkv(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+    """First phase only (the MHA split-KV kernel)."""
+    return _mha_call("mha_decode_splitkv", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
+                     metadata, buffers)
+
+
+def mha_decode_combine(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+    """Second phase only (merge of split units)."""
+    return _mha_call("mha_decode_combine", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
+                     metadata, buffers)

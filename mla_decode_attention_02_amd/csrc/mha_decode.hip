@@ -1,0 +1,419 @@
+// Paged multi-head / grouped-query decode attention (gfx950): separate K and V
+// caches [pages, 64, h_kv, d] with head size d in {64, 128, 256} and h_kv
+// dividing h_q, in the style of the key/value-cache decode call of page
+// "FlashAttention终极指南：如何通过动态计算图实现3倍推理加速" (section "核心代码实现解析":
+// q against k_cache and v_cache with cache_seqlens and a causal flag; section
+// "问题二：精度偏差处理": the LSE returned beside the output).  The work is cut
+// into (request, KV head) units by the same split-KV scheduler as the MLA path
+// and merged by LSE afterwards.
+//
+// Decode attention with a few query rows per KV head is bound by HBM bandwidth
+// (rows FLOP per byte: 8 for a group of 8 heads, against a ridge of ~312), so
+// the kernel is built to keep the K/V stream moving:
+//   * one workgroup (4 waves) per partition; K and V of KS keys of the unit's
+//     KV head stream HBM -> LDS by direct (LDS-DMA) loads into four buffers
+//     named at compile time, three steps ahead of their use;
+//   * every wave forms the scores of all KS keys for all of the workgroup's
+//     query rows (the score MFMAs are cheap at this intensity) and so runs the
+//     online softmax of every row itself: no score exchange, and after the
+//     loop no merge of per-wave states;
+//   * wave w accumulates output columns w * d_v/4 .. +d_v/4 of every row, the
+//     V^T operand coming from transposed LDS reads, the P^T operand straight
+//     from the score accumulators' registers.
+// Keys past a request's length in its last page are read over a range that
+// ends at its last valid row, so they arrive as zeros whatever the cache holds
+// there.
+#include "mla_common.hpp"
+#include "mla_internal.h"
+
+namespace mla {
+
+// 16-byte chunk swizzle of an LDS row of `cpr` chunks: rows of 256 bytes or
+// more key on row & 7 (two consecutive chunks of 8 rows then cover the 16
+// bank groups); rows of 128 bytes, two per bank row, key on (row >> 1) & 3.
+template <int CPR>
+__device__ __forceinline__ int mha_swz(int row) {
+  if constexpr (CPR >= 16) return (row & 7) << 1;
+  else return ((row >> 1) & 3) << 1;
+}
+
+// Buffer descriptor over the rows of one page and KV head; rows at or past
+// `valid` are out of range (their loads return zeros).  valid <= 0: empty.
+__device__ __forceinline__ BufRsrc mha_rows_rsrc(const void* base, int64_t elem_off, int64_t row_stride, int width,
+                                                 int valid) {
+  const int bytes = valid > 0 ? (int)(((int64_t)(valid - 1) * row_stride + width) * 2) : 0;
+  return page_rsrc((const char*)base + elem_off * 2, bytes);
+}
+
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
+  constexpr int DV = D;
+  constexpr int KS = D <= 128 ? 64 : 32;     // keys per step
+  constexpr int KT = KS / 16;                // 16-key score tiles per step
+  constexpr int SPP = kPage / KS;            // steps per page
+  constexpr int ROWB = D * 2;                // bytes of a K (and V) row in LDS
+  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  constexpr int KBYTES = KS * ROWB;
+  constexpr int BUF = 2 * KBYTES;            // K rows, then V rows
+  constexpr int DC = D / 32;                 // 32-deep contraction steps of Q.K
+  constexpr int CW = DV / 4;                 // output columns per wave
+  constexpr int CT = CW / 16;                // 16-column output tiles per wave
+  constexpr int NDMA = 2 * KBYTES / 1024 / 4;  // LDS-DMA instructions per wave and step
+  constexpr int RPI = 1024 / ROWB;           // rows per DMA instruction
+  static_assert(KT % 2 == 0 && CT >= 1 && NDMA >= 1 && 2 * KBYTES % 4096 == 0, "tile shape");
+  static_assert(3 * NDMA <= 63, "loads in flight fit the wait counter");
+  // K/V bytes are read once when the unit's rows fit one row block:
+  // non-temporal; row blocks of one unit may meet in L2 otherwise
+  constexpr int kAux = RT < 4 ? 2 : 0;
+  __shared__ __attribute__((aligned(1024))) char b0_raw[BUF];
+  __shared__ __attribute__((aligned(1024))) char b1_raw[BUF];
+  __shared__ __attribute__((aligned(1024))) char b2_raw[BUF];
+  __shared__ __attribute__((aligned(1024))) char b3_raw[BUF];
+  auto buf = [&](auto ic) -> MLA_LDS char* {
+    constexpr int i = decltype(ic)::value & 3;
+    if constexpr (i == 0) return (MLA_LDS char*)b0_raw;
+    else if constexpr (i == 1) return (MLA_LDS char*)b1_raw;
+    else if constexpr (i == 2) return (MLA_LDS char*)b2_raw;
+    else return (MLA_LDS char*)b3_raw;
+  };
+
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int mrow0 = blockIdx.y * 64;
+  const int ksw = mha_swz<CPR>(li);          // swizzle of K rows kt*16 + li
+
+  const int32_t* sc = p.sched + blockIdx.x * 8;
+  const int begin_u = ldu(sc + 0), begin_page = ldu(sc + 1);
+  const int end_u = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
+  for (int u = begin_u; u <= end_u; ++u) {
+    const int b = u / p.h_kv;
+    const int hk = u - b * p.h_kv;
+    const int n = ldu(p.seqlens + b);
+    const int npages = (n + kPage - 1) / kPage;
+    const int lo = (u == begin_u) ? begin_page : 0;
+    const int hi = (u == end_u) ? end_page : npages;
+    if (lo >= hi) continue;
+    const int split = (u == begin_u) ? begin_split : 0;
+    const int slot0 = ldu(p.split_offsets + u);
+    const int nsplit = ldu(p.split_offsets + u + 1) - slot0;
+    // steps of this chunk: its pages, less trailing steps wholly past the end
+    const int ks0 = lo * SPP;
+    const int nsteps = (min(n, hi * kPage) - lo * kPage + KS - 1) / KS;
+
+    BlockWindow bw;
+    bw.init(p.block_table + (int64_t)b * p.bt_s, lo, hi, lane);
+
+    // Q fragments (B operand of S^T = K . Q^T): row rt*16 + li, columns
+    // ks*32 + 8g .. +8; rows past the unit's rows are zero
+    u32x4 qf[RT][DC];
+    int cnt[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = mrow0 + rt * 16 + li;
+      if (row < p.rows) {
+        const int tok = row / p.group;
+        const int head = hk * p.group + (row - tok * p.group);
+        const T* qp = (const T*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2 + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) qf[rt][ks] = *(const u32x4*)(qp + ks * 32);
+        cnt[rt] = visible_count(n, p.s_q, tok, p.causal);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) qf[rt][ks] = u32x4{0, 0, 0, 0};
+        cnt[rt] = 0;
+      }
+    }
+
+    // LDS-DMA loads of step s (keys (ks0 + s) * KS ..) into buffer ic: wave w
+    // moves instructions w*NDMA .. +NDMA of the K rows then the V rows, 1 KiB
+    // (RPI rows) each; lane l fills slot l of its instruction, i.e. row
+    // j*RPI + l / CPR, chunk (l % CPR) ^ swizzle(row).  Steps past the chunk
+    // use empty descriptors, so every step issues the same loads.
+    auto issue = [&](auto ic, int s) {
+      MLA_LDS char* bp = buf(ic);
+      const bool real = s < nsteps;
+      const int kstep = ks0 + s;
+      const int page = kstep / SPP;
+      const int sub = kstep - page * SPP;
+      const int phys = real ? bw.phys(page) : 0;
+      const int valid = real ? min(kPage, n - page * kPage) : 0;
+      const BufRsrc kr = mha_rows_rsrc(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
+      const BufRsrc vr = mha_rows_rsrc(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, DV, valid);
+      int ln = lane;                             // opaque: offsets are rebuilt per step
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int j = wave * NDMA + i;           // instruction of this step, 0 .. 2*KBYTES/1024
+        const bool isv = j >= KBYTES / 1024;
+        const int jj = isv ? j - KBYTES / 1024 : j;
+        const int r = jj * RPI + ln / CPR;       // row of the step
+        const int c = (ln % CPR) ^ mha_swz<CPR>(r);
+        const int key = sub * KS + r;            // slot within the page
+        const int64_t rs = isv ? p.v_s1 : p.k_s1;
+        const int voff = (int)(key * rs * 2) + c * 16;
+        dma16<kAux>(isv ? vr : kr, bp + (isv ? KBYTES : 0) + jj * 1024, voff, 0);
+      }
+    };
+
+    float m_run[RT], l_part[RT];
+    f32x4 o[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      m_run[rt] = -INFINITY;
+      l_part[rt] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    issue(std::integral_constant<int, 2>{}, 2);
+
+    auto step = [&](auto Hc, int s) {
+      constexpr int H = decltype(Hc)::value;
+      dma_barrier<2 * NDMA>();                   // step s landed, everyone done with step s-1
+      issue(std::integral_constant<int, H + 3>{}, s + 3);
+      MLA_LDS char* kb = buf(Hc);
+      MLA_LDS char* vb = kb + KBYTES;
+      // S^T tiles: keys kt*16 + 4g .. +4 of row li of tile rt
+      f32x4 sc4[KT][RT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const MLA_LDS char* krow = kb + (kt * 16 + li) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) {
+          const u32x4 kf = ld_lds16(krow + (((ks * 4 + g) ^ ksw) << 4));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = Dt<T>::mfma32(kf, qf[rt][ks], sc4[kt][rt]);
+        }
+      }
+      // online softmax per row tile; probabilities packed as the B operand of
+      // the P.V MFMA: k-slots 8g .. 8g+7 = keys 4g..4g+3 of tiles 2kp, 2kp+1
+      u32x4 pf[RT][KT / 2];
+      float alpha[RT];
+      const int key0 = (ks0 + s) * KS + 4 * g;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float x[KT][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[kt][e] = (key0 + kt * 16 + e < cnt[rt]) ? sc4[kt][rt][e] : -INFINITY;
+            mx = fmaxf(mx, x[kt][e]);
+          }
+        mx = max_across_groups(mx) * p.scale_log2;   // scale > 0 commutes with the max
+        alpha[rt] = 1.f;
+        if (mx > m_run[rt] + kRescaleSlack) {
+          alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - mx);
+          m_run[rt] = mx;
+        }
+        const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][e], p.scale_log2, -msub));
+            rs += x[kt][e];
+          }
+        l_part[rt] = l_part[rt] * alpha[rt] + rs;
+#pragma unroll
+        for (int kp = 0; kp < KT / 2; ++kp)
+          pf[rt][kp] = u32x4{Dt<T>::pack2(x[2 * kp][0], x[2 * kp][1]), Dt<T>::pack2(x[2 * kp][2], x[2 * kp][3]),
+                             Dt<T>::pack2(x[2 * kp + 1][0], x[2 * kp + 1][1]),
+                             Dt<T>::pack2(x[2 * kp + 1][2], x[2 * kp + 1][3])};
+      }
+      bool resc = false;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) resc |= alpha[rt] != 1.f;
+      if (__any(resc)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) o[rt][ct] *= alpha[rt];
+      }
+      // O^T += V^T . P^T for this wave's columns: transposed reads of value
+      // rows 32kp + 4g + li/4 (lo) and +16 (hi), columns 4(li&3) .. +4 of the
+      // 16-column tile
+      const int vr = 4 * g + (li >> 2);
+      const int vsw = mha_swz<CPR>(vr);          // the same for vr + 16, vr + 32
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int chunk = (wave * CW + ct * 16) / 8 + ((li >> 1) & 1);
+        const int coff = ((chunk ^ vsw) << 4) + (li & 1) * 8;
+#pragma unroll
+        for (int kp = 0; kp < KT / 2; ++kp) {
+          const u32x2 lo4 = ld_lds_tr(vb + (32 * kp + vr) * ROWB + coff);
+          const u32x2 hi4 = ld_lds_tr(vb + (32 * kp + 16 + vr) * ROWB + coff);
+          const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
+        }
+      }
+    };
+    // whole groups of four steps, then the tail: every step of the loop body
+    // runs, so the compiler sees which buffer each load in flight targets
+    int s0 = 0;
+    for (; s0 + 4 <= nsteps; s0 += 4) static_for<0, 4>([&](auto Hc) { step(Hc, s0 + decltype(Hc)::value); });
+    static_for<0, 3>([&](auto Hc) {
+      const int s = s0 + decltype(Hc)::value;
+      if (s < nsteps) step(Hc, s);
+    });
+    // drain the loads issued past the end before the buffers are reused
+    dma_barrier<0>();
+
+    // epilogue: O / l, LSE; wave w writes its columns, wave 0 the LSEs
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float l = sum_across_groups(l_part[rt]);
+      const int row = mrow0 + rt * 16 + li;
+      if (row >= p.rows) continue;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float lse = l > 0.f ? (m_run[rt] + __log2f(l)) * kLn2 : -INFINITY;
+      const int tok = row / p.group;
+      const int head = hk * p.group + (row - tok * p.group);
+      if (nsplit == 1) {
+        T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + wave * CW + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const f32x4 v = o[rt][ct] * inv;
+          *(u32x2*)(dst + ct * 16) = u32x2{Dt<T>::pack2(v[0], v[1]), Dt<T>::pack2(v[2], v[3])};
+        }
+        if (wave == 0 && g == 0) p.lse[((int64_t)b * p.s_q + tok) * p.h_q + head] = lse;
+      } else {
+        const int64_t slot = slot0 + split;
+        float* dst = p.part_o + (slot * p.rows + row) * DV + wave * CW + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) *(f32x4*)(dst + ct * 16) = o[rt][ct] * inv;
+        if (wave == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- combine --
+// Merge of the split pieces of a unit by their LSE (the same identity as the
+// MLA combine): LSE = log sum_k exp(LSE_k), O = sum_k exp(LSE_k - LSE) O_k.
+// One wave per row, DV / 64 (at least 2) columns per lane; lane k holds piece k's LSE for
+// the reductions; eight pieces' loads in flight.  Units with no cached token
+// get O = 0 and LSE = -inf; unsplit units are skipped.
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void mha_combine_kernel(MhaParams p) {
+  constexpr int CPL = DV >= 128 ? DV / 64 : 2;   // columns per lane (lanes past DV / CPL idle)
+  typedef float fv __attribute__((ext_vector_type(CPL)));
+  const int u = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.y * 4 + wave;
+  if (row >= p.rows) return;
+  const int s0 = ldu(p.split_offsets + u);
+  const int ns = ldu(p.split_offsets + u + 1) - s0;
+  if (ns == 1) return;
+  const int b = u / p.h_kv, hk = u - b * p.h_kv;
+  const int tok = row / p.group;
+  const int head = hk * p.group + (row - tok * p.group);
+  const int col = min(lane * CPL, DV - CPL);      // idle lanes repeat the last columns
+  const bool writer = lane * CPL < DV;
+  fv acc;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+  float L = -INFINITY;
+  const float* lse_k = p.part_lse + (int64_t)s0 * p.rows + row;
+  const float* src = p.part_o + ((int64_t)s0 * p.rows + row) * DV + col;
+  const int64_t piece = (int64_t)p.rows * DV;
+  if (ns > 0) {
+    float mx = -INFINITY;
+    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, lse_k[(int64_t)k * p.rows]);
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
+    if (mx != -INFINITY) {
+      float sum = 0.f;
+      for (int k = lane; k < ns; k += 64) sum += __builtin_amdgcn_exp2f((lse_k[(int64_t)k * p.rows] - mx) * kLog2e);
+#pragma unroll
+      for (int sft = 32; sft >= 1; sft >>= 1) sum += __shfl_xor(sum, sft);
+      L = mx + __logf(sum);
+      for (int k0 = 0; k0 < ns; k0 += 64) {
+        const int kl = k0 + lane;
+        const float w = kl < ns ? __builtin_amdgcn_exp2f((lse_k[(int64_t)kl * p.rows] - L) * kLog2e) : 0.f;
+        const int cnt = min(64, ns - k0);
+        for (int j = 0; j < cnt; j += 8) {
+          fv v[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            if (j + t < cnt) {
+              v[t] = *(const fv*)(src + (k0 + j + t) * piece);
+            } else {
+#pragma unroll
+              for (int i = 0; i < CPL; ++i) v[t][i] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(j + t, 63)));
+            if (j + t < cnt) acc += wt * v[t];
+          }
+        }
+      }
+    }
+  }
+  T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + col;
+  if (writer) {
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2) *(uint32_t*)(dst + i) = Dt<T>::pack2(acc[i], acc[i + 1]);
+  }
+  if (lane == 0) p.lse[((int64_t)b * p.s_q + tok) * p.h_q + head] = L;
+}
+
+namespace {
+
+template <typename T, int D>
+hipError_t launch_mha_d(const MhaParams& p, hipStream_t st) {
+  const int m_blocks = (p.rows + 63) / 64;
+  const int rt = p.rows >= 64 ? 4 : (p.rows + 15) / 16;
+  const dim3 grid(p.num_parts, m_blocks);
+  switch (rt) {
+    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1>), grid, dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2>), grid, dim3(256), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3>), grid, dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4>), grid, dim3(256), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_mha_t(const MhaParams& p, int head_dim, hipStream_t st) {
+  switch (head_dim) {
+    case 64: return launch_mha_d<T, 64>(p, st);
+    case 128: return launch_mha_d<T, 128>(p, st);
+    case 256: return launch_mha_d<T, 256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_mha_combine_t(const MhaParams& p, int head_dim, hipStream_t st) {
+  const dim3 grid(p.batch * p.h_kv, (p.rows + 3) / 4);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((mha_combine_kernel<T, 64>), grid, dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((mha_combine_kernel<T, 128>), grid, dim3(256), 0, st, p); break;
+    case 256: hipLaunchKernelGGL((mha_combine_kernel<T, 256>), grid, dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mha_splitkv(const MhaParams& p, int dtype, int head_dim, hipStream_t st) {
+  return dtype == 0 ? launch_mha_t<__bf16>(p, head_dim, st) : launch_mha_t<_Float16>(p, head_dim, st);
+}
+
+hipError_t launch_mha_combine(const MhaParams& p, int dtype, int head_dim, hipStream_t st) {
+  return dtype == 0 ? launch_mha_combine_t<__bf16>(p, head_dim, st) : launch_mha_combine_t<_Float16>(p, head_dim, st);
+}
+
+}  // namespace mla

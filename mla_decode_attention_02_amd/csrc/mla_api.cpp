@@ -13,14 +13,18 @@
 #include <string>
 
 #include "../../include/mla_decode.h"
+#include "mla_api_util.h"
 #include "mla_common.hpp"
 #include "mla_internal.h"
 
 static_assert(mla::kFusedMaxPieces == MLA_FUSED_MAX_PIECES, "fused-merge limit");
 
-namespace {
+namespace mla {
+namespace api {
 
+namespace {
 thread_local std::string g_error;
+}
 
 mla_status fail(mla_status st, const char* fmt, ...) {
   char buf[512];
@@ -37,7 +41,22 @@ mla_status ok() {
   return MLA_SUCCESS;
 }
 
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+const char* last_error() { return g_error.c_str(); }
+
+}  // namespace api
+}  // namespace mla
+
+namespace {
+
+using mla::api::aligned;
+using mla::api::fail;
+using mla::api::hip_fail;
+using mla::api::ok;
+using mla::api::round256;
 
 // Query-row tile: 16 rows when everything fits one MFMA tile, else 64.
 int tile_rows(int rows) { return rows <= 16 ? 16 : 64; }
@@ -56,7 +75,6 @@ mla_status check_shape(int batch, int s_q, int h_q, int h_kv) {
 // first (their place depends on the shape only, not on num_parts), then fp32
 // partial outputs [slots, rows, 512] and their LSEs [slots, rows]; each region
 // starts on a 256-byte boundary.
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t counters_bytes(int batch, int s_q, int h_q) {
   const int rows = s_q * h_q;
@@ -153,15 +171,11 @@ mla::DecodeParams make_params(const mla_decode_args* a) {
   return p;
 }
 
-mla_status hip_fail(hipError_t e, const char* what) {
-  return fail(MLA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
-
 }  // namespace
 
 extern "C" {
 
-const char* mla_last_error(void) { return g_error.c_str(); }
+const char* mla_last_error(void) { return mla::api::last_error(); }
 
 int mla_abi_version(void) { return MLA_ABI_VERSION; }
 
@@ -198,7 +212,7 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, in
   if (!cache_seqlens || !sched || !split_offsets) return fail(MLA_ERROR_INVALID_VALUE, "NULL pointer");
   if (!aligned(cache_seqlens, 4) || !aligned(sched, 4) || !aligned(split_offsets, 4))
     return fail(MLA_ERROR_INVALID_VALUE, "int32 arrays must be 4-byte aligned");
-  hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_parts, MLA_FIXED_OVERHEAD, sched,
+  hipError_t e = mla::launch_metadata(cache_seqlens, batch, 1, num_parts, MLA_FIXED_OVERHEAD, sched,
                                       split_offsets, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "metadata launch");
   return ok();

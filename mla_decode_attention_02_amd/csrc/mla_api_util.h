@@ -1,0 +1,27 @@
+// Host-side helpers shared by the C ABI files (mla_api.cpp, mha_api.cpp): the
+// per-thread error text behind mla_last_error() and small checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mla_decode.h"
+
+namespace mla {
+namespace api {
+
+// Record a formatted message for mla_last_error() and return `st`.
+mla_status fail(mla_status st, const char* fmt, ...);
+// Clear the message and return MLA_SUCCESS.
+mla_status ok();
+// MLA_ERROR_HIP with the HIP error string.
+mla_status hip_fail(hipError_t e, const char* what);
+// The calling thread's message ("" if none).
+const char* last_error();
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace api
+}  // namespace mla

@@ -63,6 +63,31 @@ struct DecodeParams {
                             // split-KV kernel (0: never)
 };
 
+// Kernel parameters of paged multi-head / grouped-query decode (element
+// strides).  The units of work are (request, KV head) pairs, unit u = b * h_kv
+// + g; unit u has rows = s_q * group query rows (row r: token r / group, query
+// head g * group + r % group).
+struct MhaParams {
+  const void* q;
+  int64_t q_s0, q_s1, q_s2;
+  const void* k;
+  int64_t k_s0, k_s1, k_s2;  // page, slot, head
+  const void* v;
+  int64_t v_s0, v_s1, v_s2;
+  const int32_t* block_table;
+  int64_t bt_s;
+  const int32_t* seqlens;
+  const int32_t* sched;
+  const int32_t* split_offsets;
+  int batch, s_q, h_q, h_kv, group, rows, num_parts, causal;
+  float scale_log2;         // softmax_scale * log2(e)
+  void* out;
+  int64_t o_s0, o_s1, o_s2;
+  float* lse;               // [batch, s_q, h_q]
+  float* part_o;            // [slots, rows, d_v] fp32
+  float* part_lse;          // [slots, rows]
+};
+
 // Arguments of the merge of context-parallel shards (strides in elements).
 struct MergeParams {
   const void* part_out;     // shard r, request b, token, head: r*p_s0 + b*p_s1 + t*p_s2 + h*p_s3

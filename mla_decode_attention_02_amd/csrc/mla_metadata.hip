@@ -62,8 +62,10 @@ __device__ __forceinline__ int find_request(const int* C, int batch, long long p
   return lo;
 }
 
+// `batch` counts units of work here; unit b has length seqlens[b / rep].
 __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* __restrict__ seqlens, int batch,
-                                                                int num_parts, int F, int32_t* __restrict__ sched,
+                                                                int rep, int num_parts, int F,
+                                                                int32_t* __restrict__ sched,
                                                                 int32_t* __restrict__ split_offsets) {
   __shared__ int scan_s[kMetaWaves];
   __shared__ int start_s[kMetaLdsBatch + 1];
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
 
   int local = 0;
   for (int b = lo; b < hi; ++b) {
-    const int p = pages_of(seqlens[b]);
+    const int p = pages_of(seqlens[b / rep]);
     local += p > 0 ? p + F : 0;
   }
   int total;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
     int run = first;
     for (int b = lo; b < hi; ++b) {
       C[b] = run;
-      const int p = pages_of(seqlens[b]);
+      const int p = pages_of(seqlens[b / rep]);
       run += p > 0 ? p + F : 0;
     }
     if (tid == 0) C[batch] = total;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
   {
     int run = first;
     for (int b = lo; b < hi; ++b) {
-      const int p = pages_of(seqlens[b]);
+      const int p = pages_of(seqlens[b / rep]);
       nsum += pieces(run, p);
       run += p > 0 ? p + F : 0;
     }
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
   {
     int run = sfirst, start = first;
     for (int b = lo; b < hi; ++b) {
-      const int p = pages_of(seqlens[b]);
+      const int p = pages_of(seqlens[b / rep]);
       split_offsets[b] = run;
       run += pieces(start, p);
       start += p > 0 ? p + F : 0;
@@ -148,9 +150,9 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
   }
 }
 
-hipError_t launch_metadata(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead,
+hipError_t launch_metadata(const int32_t* seqlens, int units, int rep, int num_parts, int fixed_overhead,
                            int32_t* sched, int32_t* split_offsets, hipStream_t st) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMetaThreads), 0, st, seqlens, batch, num_parts,
+  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMetaThreads), 0, st, seqlens, units, rep, num_parts,
                      fixed_overhead, sched, split_offsets);
   return hipGetLastError();
 }

@@ -13,6 +13,7 @@ from mla_decode_attention_02_amd import api
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "mha_decode.h")]
 
 SUCCESS, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
 
@@ -25,9 +26,10 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(mla_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*((?:mla|mha)_[a-z_0-9]+)\s*\(", text,
+                       flags=re.M)
     return sorted(set(names))
 
 
@@ -35,7 +37,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mla_last_error", "mla_abi_version", "mla_get_metadata_shape", "mla_get_metadata",
               "mla_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
-              "mla_decode_fused"):
+              "mla_decode_fused", "mla_merge_partials", "mha_get_metadata_shape", "mha_get_metadata",
+              "mha_workspace_size", "mha_decode", "mha_decode_splitkv", "mha_decode_combine"):
         assert n in names
 
 
@@ -213,3 +216,80 @@ def test_merge_rejects_bad_arguments(L, name, brk, status):
 
 def test_merge_null_args(L):
     assert L.mla_merge_partials(None, None) == INVALID
+
+
+# ----------------------------------------------------- paged MHA / GQA --
+def test_mha_workspace_and_shape(L):
+    for batch, s_q, h_q, h_kv, d, parts in ((2, 1, 8, 2, 128, 256), (64, 1, 64, 8, 128, 256), (3, 2, 6, 1, 64, 5)):
+        n = api.mha_workspace_size(batch, s_q, h_q, h_kv, d, parts)
+        rows = s_q * (h_q // h_kv)
+        raw = (batch * h_kv + parts) * rows * (d + 1) * 4
+        assert n == (raw + 255) // 256 * 256
+    assert api.mha_get_metadata_shape(64, 1, 64, 8, num_cus=256) == (256, 256 * 8, 64 * 8 + 1)
+    assert api.mha_get_metadata_shape(2, 4, 32, 1, num_cus=256) == (128, 128 * 8, 3)     # 128 rows: 2 blocks
+    n, se, so = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert L.mha_get_metadata_shape(256, 2, 1, 6, 4, ctypes.byref(n), ctypes.byref(se), ctypes.byref(so)) == INVALID
+    assert L.mha_get_metadata(None, 2, 2, 4, 4096, 4096, None) == INVALID
+    assert L.mha_get_metadata(4096, 2, 0, 4, 4096, 4096, None) == INVALID
+
+
+def _valid_mha_args():
+    a = api.MhaArgs()
+    a.dtype = 0
+    a.batch, a.s_q, a.h_q, a.h_kv = 2, 1, 8, 2
+    a.head_dim, a.page_size = 128, 64
+    a.num_pages, a.max_pages_per_seq = 3, 2
+    base = 1 << 20
+    a.q = base
+    a.q_stride[:] = [8 * 128, 8 * 128, 128]
+    a.k_cache = base * 2
+    a.k_stride[:] = [64 * 2 * 128, 2 * 128, 128]
+    a.v_cache = base * 3
+    a.v_stride[:] = [64 * 2 * 128, 2 * 128, 128]
+    a.block_table = base * 4
+    a.bt_stride = 2
+    a.cache_seqlens = base * 5
+    a.sched = base * 6
+    a.split_offsets = base * 7
+    a.num_parts = 256
+    a.softmax_scale = 128 ** -0.5
+    a.causal = 0
+    a.workspace = base * 8
+    a.workspace_bytes = api.mha_workspace_size(2, 1, 8, 2, 128, 256)
+    a.out = base * 9
+    a.out_stride[:] = [8 * 128, 8 * 128, 128]
+    a.lse = base * 10
+    return a
+
+
+MHA_BREAKS = [
+    ("dtype", lambda a: setattr(a, "dtype", 3), UNSUPPORTED),
+    ("head_dim", lambda a: setattr(a, "head_dim", 96), UNSUPPORTED),
+    ("page_size", lambda a: setattr(a, "page_size", 32), UNSUPPORTED),
+    ("groups", lambda a: setattr(a, "h_kv", 3), INVALID),
+    ("h_kv", lambda a: setattr(a, "h_kv", 0), INVALID),
+    ("batch", lambda a: setattr(a, "batch", 0), INVALID),
+    ("num_parts", lambda a: setattr(a, "num_parts", 0), INVALID),
+    ("v null", lambda a: setattr(a, "v_cache", None), INVALID),
+    ("v misaligned", lambda a: setattr(a, "v_cache", 3 * (1 << 20) + 8), INVALID),
+    ("k stride", lambda a: a.k_stride.__setitem__(1, 100), INVALID),
+    ("slot stride small", lambda a: a.v_stride.__setitem__(1, 128), INVALID),
+    ("head stride small", lambda a: a.q_stride.__setitem__(2, 64), INVALID),
+    ("scale", lambda a: setattr(a, "softmax_scale", 0.0), INVALID),
+    ("causal", lambda a: setattr(a, "causal", 5), INVALID),
+    ("workspace small", lambda a: setattr(a, "workspace_bytes", 256), WS_SMALL),
+]
+
+
+@pytest.mark.parametrize("name,brk,status", MHA_BREAKS, ids=[b[0] for b in MHA_BREAKS])
+@pytest.mark.parametrize("entry", ["mha_decode", "mha_decode_splitkv", "mha_decode_combine"])
+def test_mha_rejects_bad_arguments(L, entry, name, brk, status):
+    a = _valid_mha_args()
+    brk(a)
+    st = getattr(L, entry)(ctypes.byref(a), None)
+    assert st == status, (name, L.mla_last_error().decode())
+    assert L.mla_last_error().decode() != ""
+
+
+def test_mha_null_args(L):
+    assert L.mha_decode(None, None) == INVALID
