@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
 SOURCES = ["mla_api.cpp", "mha_api.cpp", "mla_metadata.hip", "mla_splitkv_wide.hip", "mla_splitkv_narrow.hip",
-           "mla_combine.hip", "mla_merge.hip", "mha_decode.hip"]
+           "mla_splitkv_fp8.hip", "mla_combine.hip", "mla_merge.hip", "mha_decode.hip"]
 ARCH = "gfx950"
 
 

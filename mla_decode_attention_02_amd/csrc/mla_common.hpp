@@ -239,11 +239,6 @@ __device__ __forceinline__ u32x4 buf_load16(BufRsrc r, int voff, int soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAux));
 }
 
-template <int kAux>
-__device__ __forceinline__ u32x2 buf_load8(BufRsrc r, int voff, int soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAux));
-}
-
 // Issue the loads of one 64x576 page (HBM -> registers).  Wave w fetches value
 // rows 16w..16w+15 (one 1 KiB row per instruction, fully coalesced) and rope
 // rows 16w..16w+15 (8 rows per instruction).  Lane l fetches the source chunk
@@ -261,59 +256,6 @@ __device__ __forceinline__ void stage_load(PageStage& st, BufRsrc page, int row_
     const int voff = (lane >> 3) * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
     st.v[16 + i] = buf_load16<kAux>(page, voff, (wave * 2 + i) * 8 * row_bytes);
   }
-}
-
-// ----------------------------------------------------------- fp8 pages --
-// A page of fp8 e4m3 codes (576 bytes per cached row) staged in registers: the
-// same rows and 16-byte LDS slots as PageStage, but each lane fetches the 8
-// codes that convert into its slot (8 bytes per row and lane).  The page's
-// scale travels with it; the kernels apply it to the scores and to the
-// probabilities, not to the codes, so any finite scale is exact.
-struct PageStage8 {
-  u32x2 v[18];
-  float scale;
-};
-
-// Scale of page `phys`, read through the vector memory path: it completes in
-// order with the page loads around it, so an LDS wait (which shares its
-// counter with scalar loads) never waits for it.  The load is always issued,
-// over an empty range (reading 0) when there is no scale array or no page, so
-// that every step issues the same number of loads; the caller substitutes 1
-// for a missing array where it uses the value.
-__device__ __forceinline__ float page_scale(const float* k_scale, int phys, bool live) {
-  const BufRsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(k_scale), (short)0,
-                                                      k_scale && live ? 0x7FFFFFFF : 0, 0x00020000);
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, phys * 4, 0));
-}
-
-template <int kAux>
-__device__ __forceinline__ void stage_load8(PageStage8& st, BufRsrc page, float scale, int row_bytes, int wave,
-                                            int lane) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int key = (j & 7) << 1;                          // == swz_v(16 * wave + j)
-    st.v[j] = buf_load8<kAux>(page, (lane ^ key) << 3, (wave * 16 + j) * row_bytes);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (wave * 2 + i) * 8 + (lane >> 3);
-    const int voff = (lane >> 3) * row_bytes + 512 + (((lane & 7) ^ swz_r(r)) << 3);
-    st.v[16 + i] = buf_load8<kAux>(page, voff, (wave * 2 + i) * 8 * row_bytes);
-  }
-  st.scale = scale;
-}
-
-// Eight e4m3 codes -> their eight values in bf16.  Every e4m3 value (3
-// mantissa bits, exponents -9 .. 8) is a bf16 value, so this is exact; the
-// gfx950 conversion is used with a unit scale.
-__device__ __forceinline__ u32x4 codes_to_bf16(u32x2 w) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
-  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
-               __builtin_bit_cast(uint32_t, d)};
 }
 
 // Physical page numbers of one request, fetched 64 at a time with a single
@@ -421,15 +363,6 @@ __device__ __forceinline__ void stage_store(const PageStage& st, MLA_LDS char* b
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     *(MLA_LDS u32x4*)(buf + kRopeOff + (wave * 2 + i) * 1024 + lane * 16) = st.v[16 + i];
-}
-
-__device__ __forceinline__ void stage_store8(const PageStage8& st, MLA_LDS char* buf, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    *(MLA_LDS u32x4*)(buf + (wave * 16 + j) * 1024 + lane * 16) = codes_to_bf16(st.v[j]);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    *(MLA_LDS u32x4*)(buf + kRopeOff + (wave * 2 + i) * 1024 + lane * 16) = codes_to_bf16(st.v[16 + i]);
 }
 
 // Compile-time unrolled loop: f(std::integral_constant<int, I>) for I in [B, E).

@@ -85,10 +85,6 @@ __device__ __forceinline__ void for_each_chunk(const DecodeParams& p, F&& f) {
 __device__ __forceinline__ BufRsrc page_of(const DecodeParams& p, int phys, int page_bytes) {
   return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0 * 2, page_bytes);
 }
-// The same for a cache of fp8 codes (one byte per element).
-__device__ __forceinline__ BufRsrc page_of8(const DecodeParams& p, int phys, int page_bytes) {
-  return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0, page_bytes);
-}
 
 // --------------------------------------------------------- fused merge --
 // The combine folded into the split-KV kernel (the MI355X answer to launching

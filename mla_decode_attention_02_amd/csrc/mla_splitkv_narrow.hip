@@ -1,24 +1,18 @@
 // Split-KV MLA decode attention, narrow tile (up to 16 query rows per workgroup).
 // Built with MFMA accumulators in VGPR form: the per-wave output rescale runs on
 // them with plain VALU instructions, without AGPR round trips.
-// With KV8 the cache holds fp8 e4m3 codes and a scale per page: pages are
-// staged as codes (half the bytes) and converted to bf16 on their way into LDS,
-// exactly; the page's scale c enters as S = c * (q . codes) and as the value
-// operand c * P (the softmax denominator sums the unscaled P), which is
-// K = c * codes without rounding c * code to bf16.
 #include "mla_splitkv.hpp"
 
 namespace mla {
 
 // ---------------------------------------------------------------- narrow --
-template <typename T, bool KV8>
+template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char kbuf0_raw[kPageBytes];
   __shared__ __attribute__((aligned(1024))) char kbuf1_raw[kPageBytes];
   __shared__ float m_w[kWaves][16];
   __shared__ float l_w[kWaves][16];
   __shared__ MergeLds<16> merge_s;
-  __shared__ float ksc_s[2];                              // fp8: scale of the page in kbuf0 / kbuf1
   MLA_LDS char* kbuf0 = (MLA_LDS char*)kbuf0_raw;
   MLA_LDS char* kbuf1 = (MLA_LDS char*)kbuf1_raw;
   constexpr int kMergeStride = kDV + 4;   // floats per row of the merge buffer
@@ -26,39 +20,8 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
 
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int esize = KV8 ? 1 : 2;                          // bytes per cached element
-  const int row_bytes = (int)(p.k_s1 * esize);
-  const int page_bytes = (kPage - 1) * row_bytes + kDK * esize;
-  using Stage = std::conditional_t<KV8, PageStage8, PageStage>;
-  // Loads of page pg of the chunk into a register stage, and their LDS store.
-  // A load past the chunk's last page is issued over an empty range (it reads
-  // zeros without touching memory).  The fp8 kernel always issues its loads
-  // that way: every step then issues the same number of loads, so the
-  // compiler's wait before a stage's LDS store counts the next page's loads
-  // as younger and does not wait for them (measured 7% faster there; the bf16
-  // kernel, whose steps are bound by HBM bandwidth, gains nothing and loses on
-  // short chunks, so it skips such loads).
-  auto load = [&](Stage& st, BlockWindow& bw, int pg, int hi) __attribute__((always_inline)) {
-    const bool live = pg < hi;
-    const int phys = bw.phys(live ? pg : hi - 1);
-    const int bytes = live ? page_bytes : 0;
-    if constexpr (KV8) {
-      stage_load8<kNarrowAux>(st, page_of8(p, phys, bytes), page_scale(p.k_scale, phys, live), row_bytes, wave,
-                              lane);
-    } else {
-      stage_load<kNarrowAux>(st, page_of(p, phys, bytes), row_bytes, wave, lane);
-    }
-  };
-  // the page's scale goes to LDS with the page, so no register holds it across
-  // the two steps between its load and its use
-  auto store = [&](const Stage& st, MLA_LDS char* buf, int slot) __attribute__((always_inline)) {
-    if constexpr (KV8) {
-      stage_store8(st, buf, wave, lane);
-      if (tid == 0) ksc_s[slot] = st.scale;
-    } else {
-      stage_store(st, buf, wave, lane);
-    }
-  };
+  const int row_bytes = (int)(p.k_s1 * 2);
+  const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
 
   for_each_chunk(p, [&](const Chunk& c) {
     BlockWindow bw;
@@ -78,16 +41,14 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
     const int vh = (li >> 1) & 1;
 
     // two pages in flight in registers while a third is read from LDS
-    Stage st[2];
-    load(st[0], bw, c.lo, c.hi);
-    if (KV8 || c.lo + 1 < c.hi) load(st[1], bw, c.lo + 1, c.hi);
-    store(st[0], kbuf0, 0);
+    PageStage st[2];
+    stage_load<kNarrowAux>(st[0], page_of(p, bw.phys(c.lo), page_bytes), row_bytes, wave, lane);
+    if (c.lo + 1 < c.hi) stage_load<kNarrowAux>(st[1], page_of(p, bw.phys(c.lo + 1), page_bytes), row_bytes, wave, lane);
+    stage_store(st[0], kbuf0, wave, lane);
     lds_barrier();
     page_loop(c.lo, c.hi, kbuf0, kbuf1, [&](auto par, MLA_LDS char* cur, MLA_LDS char* nxt, int pg) {
       constexpr int P = decltype(par)::value;   // st[P] held page pg, st[P ^ 1] holds pg + 1
-      float ksc = 1.f;                          // page pg's scale (fp8 cache)
-      if constexpr (KV8) ksc = p.k_scale ? ksc_s[P] : 1.f;
-      if (KV8 || pg + 2 < c.hi) load(st[P], bw, pg + 2, c.hi);
+      if (pg + 2 < c.hi) stage_load<kNarrowAux>(st[P], page_of(p, bw.phys(pg + 2), page_bytes), row_bytes, wave, lane);
 
       // S^T for keys wave*16 .. +16 of the page, all 16 rows; operand reads
       // run two steps ahead of the MFMAs
@@ -104,7 +65,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float t = (key0 + r < cnt) ? s[r] * (p.scale_log2 * ksc) : -INFINITY;
+        const float t = (key0 + r < cnt) ? s[r] * p.scale_log2 : -INFINITY;
         s[r] = t;
         mx = fmaxf(mx, t);
       }
@@ -126,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
 #pragma unroll
         for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
       }
-      const u32x2 pk = {Dt<T>::pack2(s[0] * ksc, s[1] * ksc), Dt<T>::pack2(s[2] * ksc, s[3] * ksc)};
+      const u32x2 pk = {Dt<T>::pack2(s[0], s[1]), Dt<T>::pack2(s[2], s[3])};
       constexpr int kAhead = 4;
       u32x2 vf[kAhead + 1];
       auto vaddr = [&](int ct) { return cur + vbase + (ct >> 3) * 256 + ((((2 * ct) & 15) + vh) ^ vkey) * 16; };
@@ -137,7 +98,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
         if (ct + kAhead < 32) vf[(ct + kAhead) % (kAhead + 1)] = ld_lds_tr(vaddr(ct + kAhead));
         o[ct] = Dt<T>::mfma16(vf[ct % (kAhead + 1)], pk, o[ct]);
       }
-      if (pg + 1 < c.hi) store(st[P ^ 1], nxt, P ^ 1);
+      if (pg + 1 < c.hi) stage_store(st[P ^ 1], nxt, wave, lane);
       lds_barrier();
     });
 
@@ -199,9 +160,9 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
 }
 
 hipError_t launch_splitkv_narrow(const DecodeParams& p, int dtype, hipStream_t st) {
-  if (p.kv_fp8) hipLaunchKernelGGL((splitkv_narrow_kernel<__bf16, true>), dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
-  else if (dtype == 0) hipLaunchKernelGGL((splitkv_narrow_kernel<__bf16, false>), dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
-  else hipLaunchKernelGGL((splitkv_narrow_kernel<_Float16, false>), dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
+  if (p.kv_fp8) return launch_splitkv_fp8(p, st);   // fp8 cache: mla_splitkv_fp8.hip
+  if (dtype == 0) hipLaunchKernelGGL(splitkv_narrow_kernel<__bf16>, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
+  else hipLaunchKernelGGL(splitkv_narrow_kernel<_Float16>, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
