@@ -43,8 +43,16 @@ CSRC = os.path.join(ROOT, "mla_decode_attention_02_amd", "csrc")
 KERNEL_SOURCES = {
     "splitkv_wide_kernel": ["mla_splitkv_wide.hip", "mla_splitkv.hpp", "mla_common.hpp"],
     "splitkv_narrow_kernel": ["mla_splitkv_narrow.hip", "mla_splitkv.hpp", "mla_common.hpp"],
+    "splitkv_fp8_kernel": ["mla_splitkv_fp8.hip", "mla_splitkv.hpp", "mla_common.hpp"],
     "mha_splitkv_kernel": ["mha_decode.hip", "mla_common.hpp"],
 }
+
+
+def mla_kernel_name(w) -> str:
+    """The split-KV kernel that runs a workload."""
+    if w.kv == "fp8":
+        return "splitkv_fp8_kernel"
+    return "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
 COPY_MIB = 1024
 
 
@@ -89,7 +97,7 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
 
     mha = workload in MHA_WORKLOADS
     w = MHA_WORKLOADS[workload] if mha else WORKLOADS[workload]
-    kernel = "mha_splitkv_kernel" if mha else ("splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel")
+    kernel = "mha_splitkv_kernel" if mha else mla_kernel_name(w)
     tag = f"w{workload}"
     stats = _counter_rows(os.path.join(out_dir, f"prof_{tag}", f"{tag}_kernel_stats.csv"))
 
@@ -436,7 +444,7 @@ def main() -> int:
         ach = flops / (splitkv_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
+    roof["kernel"] = mla_kernel_name(w)
     # HBM bytes per launch measured by the committed counters (null if stale)
     roof["traffic"] = stored_traffic(roof["kernel"], w.name)
     roof["kernel_avg_us"] = round(splitkv_avg * 1e3, 2)
