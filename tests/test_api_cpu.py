@@ -1,0 +1,43 @@
+"""The binding fails loudly, before any compute, on inputs the library cannot
+take: host tensors, mismatched dtypes or shapes.  There is no CPU fallback."""
+
+import pytest
+import torch
+
+from mla_decode_attention_02_amd import api
+from mla_decode_attention_02_amd.workloads import make_inputs, make_mha_inputs
+
+
+def test_mla_rejects_host_tensors():
+    x = make_inputs(2, 1, 16, "bf16", seqlens=(64, 3), seed=1)
+    with pytest.raises(ValueError):
+        api.mla_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, False,
+                       metadata=(torch.zeros(4, 8, dtype=torch.int32), torch.zeros(3, dtype=torch.int32)))
+
+
+def test_mla_rejects_dtype_mismatch():
+    x = make_inputs(2, 1, 16, "bf16", seqlens=(64, 3), seed=1)
+    with pytest.raises(ValueError):
+        api._validate_tensors(x.q, x.k_cache.half(), x.block_table, x.cache_seqlens)
+    with pytest.raises(ValueError):
+        api._validate_tensors(x.q.half(), x.k_cache.to(torch.float8_e4m3fn), x.block_table, x.cache_seqlens)
+    with pytest.raises(ValueError):                    # a scale array needs an fp8 cache
+        api._validate_tensors(x.q, x.k_cache, x.block_table, x.cache_seqlens,
+                              k_scale=torch.ones(x.k_cache.shape[0]))
+
+
+def test_mha_rejects_mismatches():
+    x = make_mha_inputs(2, 1, 8, 2, 64, "bf16", seqlens=(64, 3), seed=1)
+    with pytest.raises(ValueError):
+        api._validate_mha(x.q, x.k_cache, x.v_cache.half(), x.block_table, x.cache_seqlens)
+    with pytest.raises(ValueError):
+        api._validate_mha(x.q, x.k_cache, x.v_cache[..., :32], x.block_table, x.cache_seqlens)
+    with pytest.raises(ValueError):                    # host tensors
+        api._validate_mha(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens)
+
+
+def test_metadata_needs_device_lengths():
+    with pytest.raises(ValueError):
+        api.get_metadata(torch.tensor([3, 4], dtype=torch.int32), 1, 16)
+    with pytest.raises(ValueError):
+        api.mha_get_metadata(torch.tensor([3, 4], dtype=torch.int32), 1, 8, 2)

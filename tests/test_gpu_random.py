@@ -1,0 +1,107 @@
+"""Seeded random shapes against the oracle (GPU): a sweep over batch, s_q,
+h_q, lengths, causal, dtype and partition counts for the MLA path (bf16/fp16
+and fp8 caches) and the MHA path.  Each case prints its parameters first."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dequantize_cache, oracle_decode, oracle_mha_decode
+from mla_decode_attention_02_amd import api
+from mla_decode_attention_02_amd.workloads import make_inputs, make_mha_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE = 1.5e-2, 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _compare(out, lse, ref_o, ref_l, tag):
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(lse)), f"{tag}: -inf pattern differs"
+    assert np.abs(out - ref_o).max() <= TOL_O, f"{tag}: max|dO| = {np.abs(out - ref_o).max()}"
+    if fin.any():
+        assert np.abs(lse[fin] - ref_l[fin]).max() <= TOL_LSE, f"{tag}: LSE"
+
+
+def _case(rng, max_rows):
+    B = int(rng.integers(1, 6))
+    s_q = int(rng.integers(1, 4))
+    h_q = int(rng.integers(1, max(2, max_rows // s_q) + 1))
+    seqlens = tuple(int(x) for x in rng.integers(0, 700, size=B))
+    causal = bool(rng.integers(0, 2))
+    parts = int(rng.integers(1, 40))
+    return B, s_q, h_q, seqlens, causal, parts
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mla_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B, s_q, h_q, seqlens, causal, parts = _case(rng, 160)
+    dtype = "bf16" if rng.integers(0, 2) else "fp16"
+    tag = f"mla seed={seed} B={B} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {dtype} parts={parts}"
+    _say(tag)
+    x = make_inputs(B, s_q, h_q, dtype, seqlens=seqlens, causal=causal, seed=seed, poison=True, extra_pages=1)
+    g = x.to(torch.device("cuda:0"))
+    meta = api.get_metadata(g.cache_seqlens, s_q, h_q, num_parts=parts)
+    out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale, causal, metadata=meta)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+    _compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fp8_random(seed):
+    rng = np.random.default_rng(2000 + seed)
+    B, s_q, h_q, seqlens, causal, parts = _case(rng, 16)
+    mode = ["amax", "pow2", "none"][int(rng.integers(0, 3))]
+    tag = f"fp8 seed={seed} B={B} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {mode} parts={parts}"
+    _say(tag)
+    x = make_inputs(B, s_q, h_q, "bf16", seqlens=seqlens, causal=causal, seed=seed, poison=True, extra_pages=1,
+                    kv_dtype="fp8", scale_mode=mode)
+    g = x.to(torch.device("cuda:0"))
+    meta = api.get_metadata(g.cache_seqlens, s_q, h_q, num_parts=parts)
+    out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale, causal, metadata=meta,
+                              k_scale=g.k_scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(x.q, dequantize_cache(x.k_cache, x.k_scale), x.block_table, x.cache_seqlens,
+                                 x.softmax_scale, causal)
+    _compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mha_random(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B, s_q, _, seqlens, causal, parts = _case(rng, 8)
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    d = int(rng.choice([64, 128, 256]))
+    dtype = "bf16" if rng.integers(0, 2) else "fp16"
+    h_q = h_kv * group
+    tag = f"mha seed={seed} B={B} s_q={s_q} h_q={h_q} h_kv={h_kv} d={d} seqlens={seqlens} causal={causal} {dtype} parts={parts}"
+    _say(tag)
+    x = make_mha_inputs(B, s_q, h_q, h_kv, d, dtype, seqlens=seqlens, causal=causal, seed=seed, poison=True,
+                        extra_pages=1)
+    g = x.to(torch.device("cuda:0"))
+    meta = api.mha_get_metadata(g.cache_seqlens, s_q, h_q, h_kv, num_parts=parts)
+    out, lse = api.mha_decode(g.q, g.k_cache, g.v_cache, g.block_table, g.cache_seqlens, g.softmax_scale, causal,
+                              metadata=meta)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, x.softmax_scale,
+                                     causal)
+    _compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag)
