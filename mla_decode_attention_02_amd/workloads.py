@@ -223,11 +223,14 @@ class MhaInputs:
     softmax_scale: float
     causal: bool
     dtype: str
+    k_scale: Optional[torch.Tensor] = None       # fp8 caches: [num_pages, h_kv] fp32
+    v_scale: Optional[torch.Tensor] = None
 
     def to(self, device) -> "MhaInputs":
+        mv = lambda t: None if t is None else t.to(device)
         return MhaInputs(self.q.to(device), self.k_cache.to(device), self.v_cache.to(device),
                          self.block_table.to(device), self.cache_seqlens.to(device),
-                         self.softmax_scale, self.causal, self.dtype)
+                         self.softmax_scale, self.causal, self.dtype, mv(self.k_scale), mv(self.v_scale))
 
 
 @dataclass(frozen=True)
@@ -243,6 +246,7 @@ class MhaWorkload:
     seqlens: Optional[Sequence[int]] = None
     seqlen_range: Optional[tuple] = None
     seed: int = 0
+    kv: str = "same"
     description: str = field(default="", compare=False)
 
 
@@ -253,6 +257,9 @@ MHA_WORKLOADS = {
                    description="B64 s_q1 h_q64 h_kv8 d128 bf16, s_k ~ U[1,8192]"),
     8: MhaWorkload("gqa_longctx_bs8_hq32_hkv8_d128", 8, 1, 32, 8, 128, "bf16", False, seqlens=(32768,) * 8,
                    seed=8, description="B8 s_q1 h_q32 h_kv8 d128 bf16, every s_k 32768"),
+    9: MhaWorkload("gqa_bs64_hq64_hkv8_d128_fp8kv", 64, 1, 64, 8, 128, "bf16", False, seqlen_range=(1, 8192),
+                   seed=7, kv="fp8",
+                   description="workload 7 with fp8 e4m3 K/V caches, one scale per page and KV head"),
 }
 
 
@@ -262,15 +269,23 @@ def make_mha_inputs(batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int, dt
                     seqlen_range: Optional[tuple] = None,
                     sigma: float = 1.0, causal: bool = False, seed: int = 0,
                     extra_pages: int = 0, poison: bool = False,
-                    max_pages: Optional[int] = None) -> MhaInputs:
+                    max_pages: Optional[int] = None, kv_dtype: str = "same",
+                    scale_mode: str = "amax") -> MhaInputs:
     """Seeded MHA/GQA decode inputs.  Same recipe as make_inputs, with the
     draws in the order: lengths, page permutation, q [B,s_q,h_q,d],
     k [N,64,h_kv,d], v [N,64,h_kv,d_v] (each torch.randn * sigma), then the cast
     to the dtype.  Poison (correctness runs): slots past a request's length in
     its last page and every unused page get K = +-POISON along the sign of the
-    first query row of the KV head's group and V = POISON."""
+    first query row of the KV head's group and V = POISON.  fp8 caches
+    (kv_dtype="fp8", bf16 q): K and V are drawn and poisoned in fp32, then
+    encoded per page and KV head as for the MLA cache (scale = amax / 448, or
+    its power-of-two ceiling, or no scale array), scales [num_pages, h_kv]."""
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+    if kv_dtype not in ("same", "fp8"):
+        raise ValueError("kv_dtype must be 'same' or 'fp8'")
+    if kv_dtype == "fp8" and dtype != "bf16":
+        raise ValueError("fp8 caches go with a bf16 q")
     if h_q % h_kv != 0:
         raise ValueError("h_q must be a multiple of h_kv")
     d_v = head_dim if head_dim_v is None else head_dim_v
@@ -300,8 +315,9 @@ def make_mha_inputs(batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int, dt
         pos += p
     tdt = _DTYPES[dtype]
     q = (torch.randn(batch, s_q, h_q, head_dim, generator=g) * sigma).to(tdt)
-    k = (torch.randn(max(total, 1), PAGE, h_kv, head_dim, generator=g) * sigma).to(tdt)
-    v = (torch.randn(max(total, 1), PAGE, h_kv, d_v, generator=g) * sigma).to(tdt)
+    kdt = torch.float32 if kv_dtype == "fp8" else tdt
+    k = (torch.randn(max(total, 1), PAGE, h_kv, head_dim, generator=g) * sigma).to(kdt)
+    v = (torch.randn(max(total, 1), PAGE, h_kv, d_v, generator=g) * sigma).to(kdt)
     if poison:
         group = h_q // h_kv
         for b in range(batch):
@@ -312,18 +328,36 @@ def make_mha_inputs(batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int, dt
                 for hk in range(h_kv):
                     direction = torch.sign(q[b, 0, hk * group].float())
                     direction[direction == 0] = 1.0
-                    k[page, n % PAGE:, hk, :] = (direction * POISON).to(tdt)
+                    k[page, n % PAGE:, hk, :] = (direction * POISON).to(kdt)
                 v[page, n % PAGE:] = POISON
         if total > used:
             k[perm[used:]] = POISON
             v[perm[used:]] = POISON
+    k_scale = v_scale = None
+    if kv_dtype == "fp8":
+        k, k_scale = _encode_fp8_heads(k, scale_mode)
+        v, v_scale = _encode_fp8_heads(v, scale_mode)
     return MhaInputs(q=q, k_cache=k, v_cache=v, block_table=bt, cache_seqlens=sl.to(torch.int32),
-                     softmax_scale=1.0 / (head_dim ** 0.5), causal=causal, dtype=dtype)
+                     softmax_scale=1.0 / (head_dim ** 0.5), causal=causal, dtype=dtype,
+                     k_scale=k_scale, v_scale=v_scale)
+
+
+def _encode_fp8_heads(x: torch.Tensor, scale_mode: str):
+    """fp32 cache [N, 64, h, d] -> (e4m3fn codes, scales [N, h] or None)."""
+    if scale_mode == "none":
+        return x.clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn), None
+    amax = x.abs().amax(dim=(1, 3)).clamp_min(1e-30)
+    scale = amax / FP8_MAX
+    if scale_mode == "pow2":
+        scale = torch.exp2(torch.ceil(torch.log2(scale)))
+    codes = (x / scale[:, None, :, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes, scale.to(torch.float32).contiguous()
 
 
 def mha_workload_inputs(index: int, poison: bool = False, **overrides) -> MhaInputs:
     w = MHA_WORKLOADS[int(index)]
-    kw = dict(seqlens=w.seqlens, seqlen_range=w.seqlen_range, causal=w.causal, seed=w.seed, poison=poison)
+    kw = dict(seqlens=w.seqlens, seqlen_range=w.seqlen_range, causal=w.causal, seed=w.seed, poison=poison,
+              kv_dtype=w.kv)
     kw.update(overrides)
     return make_mha_inputs(w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim, w.dtype, **kw)
 

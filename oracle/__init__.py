@@ -30,5 +30,5 @@ from .decode import (  # noqa: F401
     PAGE,
 )
 from .metadata import oracle_metadata, schedule_chunks  # noqa: F401
-from .fp8 import decode_e4m3fn, dequantize_cache, e4m3fn_value  # noqa: F401
+from .fp8 import decode_e4m3fn, dequantize_cache, dequantize_heads, e4m3fn_value  # noqa: F401
 from .mha import brute_force_mha, oracle_mha_decode, oracle_mha_metadata, oracle_mha_rows  # noqa: F401

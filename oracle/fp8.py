@@ -17,7 +17,9 @@ as fp8 codes in the OCP e4m3 "fn" encoding (1 sign bit, 4 exponent bits with
 bias 7, 3 mantissa bits; exponent field 0 is subnormal; no infinities; the two
 codes with every exponent and mantissa bit set are NaN) with one fp32 scale
 per 64-token page: the cached value is code value * scale[page].  q stays bf16
-and the attention is the one of decode.py over those values.
+and the attention is the one of decode.py over those values.  For the separate
+K and V caches of the multi-head path (mha.py) the same encoding carries one
+scale per page and KV head (dequantize_heads).
 """
 
 from __future__ import annotations
@@ -88,3 +90,23 @@ def dequantize_cache(codes, k_scale=None) -> np.ndarray:
     if s.shape != (v.shape[0],):
         raise ValueError("k_scale must hold one scale per page")
     return v * s.reshape((-1,) + (1,) * (v.ndim - 1))
+
+
+def dequantize_heads(codes, scale=None) -> np.ndarray:
+    """fp8 cache [num_pages, 64, h_kv, d] of codes and scales [num_pages, h_kv]
+    (one per page and KV head; None: every scale is 1) -> float64 cache of the
+    same shape holding code value * scale[page, head]."""
+    v = decode_e4m3fn(codes)
+    if scale is None:
+        return v
+    try:
+        import torch
+
+        if isinstance(scale, torch.Tensor):
+            scale = scale.detach().cpu().to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    s = np.asarray(scale, dtype=np.float64)
+    if s.shape != (v.shape[0], v.shape[2]):
+        raise ValueError("scale must hold one value per page and KV head")
+    return v * s[:, None, :, None]

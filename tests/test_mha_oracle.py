@@ -142,3 +142,33 @@ def test_unit_schedule_is_the_request_schedule_of_the_repeated_lengths():
     s2, o2 = oracle_metadata([5, 5, 5, 0, 0, 0, 300, 300, 300, 64, 64, 64], 7)
     assert np.array_equal(s1, s2) and np.array_equal(o1, o2)
     assert o1.shape == (13,)
+
+
+def test_fp8_heads_scale_per_page_and_head():
+    from oracle import decode_e4m3fn, dequantize_heads
+
+    codes = np.full((3, 64, 2, 8), 0x38, dtype=np.uint8)      # every value 1.0
+    scale = np.array([[0.5, 2.0], [3.0, 0.25], [1.0, 7.0]], dtype=np.float32)
+    x = dequantize_heads(codes, scale)
+    for p_ in range(3):
+        for h in range(2):
+            assert np.all(x[p_, :, h, :] == float(scale[p_, h]))
+    assert np.array_equal(dequantize_heads(codes, None), decode_e4m3fn(codes))
+    with pytest.raises(ValueError):
+        dequantize_heads(codes, scale[:, :1])
+
+
+@pytest.mark.parametrize("mode", ["amax", "pow2", "none"])
+def test_fp8_mha_generator_within_rounding(mode):
+    from oracle import dequantize_heads
+
+    kw = dict(seqlens=(100, 3), seed=5, extra_pages=1)
+    x8 = make_mha_inputs(2, 1, 8, 2, 64, "bf16", kv_dtype="fp8", scale_mode=mode, **kw)
+    xb = make_mha_inputs(2, 1, 8, 2, 64, "bf16", **kw)
+    assert torch.equal(x8.q, xb.q)
+    for c8, s8, cb in ((x8.k_cache, x8.k_scale, xb.k_cache), (x8.v_cache, x8.v_scale, xb.v_cache)):
+        vals = dequantize_heads(c8, s8)
+        ref = cb.double().numpy()
+        s = np.ones((vals.shape[0], vals.shape[2])) if s8 is None else s8.double().numpy()
+        bound = (2.0 ** -4 + 2.0 ** -8) * np.abs(ref) + s[:, None, :, None] * 2.0 ** -9
+        assert np.all(np.abs(vals - ref) <= bound)
