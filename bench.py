@@ -124,7 +124,8 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
         from mla_decode_attention_02_amd.workloads import workload_seqlens
         seqlens = workload_seqlens(workload)
     if mha:
-        flops, kv, qb, ob, lseb, tb = mha_algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim)
+        flops, kv, qb, ob, lseb, tb = mha_algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim,
+                                                             kv_elem=1 if w.kv == "fp8" else 2)
     else:
         flops, kv, qb, ob, lseb, tb = algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q,
                                                          kv_elem=1 if w.kv == "fp8" else 2)
@@ -187,13 +188,16 @@ def algorithmic_counts(seqlens, batch, s_q, h_q, elem=2, kv_elem=2):
     return flops, kv, q, o, lse, tables
 
 
-def mha_algorithmic_counts(seqlens, batch, s_q, h_q, h_kv, d):
+def mha_algorithmic_counts(seqlens, batch, s_q, h_q, h_kv, d, kv_elem=2):
     """FLOPs and bytes of one paged MHA/GQA decode step, from the definition:
     FLOPs = sum_b 2*s_q*h_q*s_k,b*(d + d); bytes = K and V rows of every KV head
-    once (2*h_kv*d*2 per token) + Q + O + LSE + table entries and lengths."""
+    once (2*h_kv*d*kv_elem per token; an fp8 cache adds its two 4-byte scales
+    per page and KV head) + Q + O + LSE + table entries and lengths."""
     rows = s_q * h_q
     flops = sum(2.0 * rows * n * (d + d) for n in seqlens)
-    kv = sum(n * h_kv * d * 2 * 2 for n in seqlens)
+    kv = sum(n * h_kv * d * 2 * kv_elem for n in seqlens)
+    if kv_elem == 1:
+        kv += sum((n + PAGE - 1) // PAGE for n in seqlens) * h_kv * 2 * 4
     q = batch * rows * d * 2
     o = batch * rows * d * 2
     lse = batch * rows * 4
@@ -211,7 +215,8 @@ def bench_mha(args) -> dict:
     w = MHA_WORKLOADS[args.workload]
     host = mha_workload_inputs(args.workload)
     seqlens = host.cache_seqlens.tolist()
-    flops, kv, qb, ob, lseb, tb = mha_algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim)
+    flops, kv, qb, ob, lseb, tb = mha_algorithmic_counts(seqlens, w.batch, w.s_q, w.h_q, w.h_kv, w.head_dim,
+                                                         kv_elem=1 if w.kv == "fp8" else 2)
     step_bytes = kv + qb + ob + lseb + tb
     splitkv_bytes = kv + qb + tb
     g = host.to(torch.device("cuda:0"))
@@ -227,10 +232,12 @@ def bench_mha(args) -> dict:
         k, v = caches[i % len(caches)]
         if ev is not None:
             ev[0].record()
-        api.mha_decode_splitkv(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+        api.mha_decode_splitkv(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
+                               g.k_scale, g.v_scale)
         if ev is not None:
             ev[1].record()
-        api.mha_decode_combine(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs)
+        api.mha_decode_combine(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
+                               g.k_scale, g.v_scale)
 
     for i in range(args.warmup):
         step(i)
@@ -266,7 +273,8 @@ def bench_mha(args) -> dict:
         "data": "synthetic: seeded randn q/K/V, shuffled 64-token page table",
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
                    "head_dim": w.head_dim, "s_k": w.description, "page": PAGE, "causal": w.causal,
-                   "num_parts": num_parts, "kv_copies": len(caches)},
+                   "num_parts": num_parts, "kv_copies": len(caches),
+                   "kv_cache": "fp8_e4m3 + fp32 scale per page and KV head" if w.kv == "fp8" else w.dtype},
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,
     }
@@ -274,7 +282,12 @@ def bench_mha(args) -> dict:
         import numpy as np
         from oracle.mha import oracle_mha_rows
 
-        qf, kf, vf = host.q.double().numpy(), host.k_cache.double().numpy(), host.v_cache.double().numpy()
+        qf = host.q.double().numpy()
+        if w.kv == "fp8":
+            from oracle import dequantize_heads
+            kf, vf = dequantize_heads(host.k_cache, host.k_scale), dequantize_heads(host.v_cache, host.v_scale)
+        else:
+            kf, vf = host.k_cache.double().numpy(), host.v_cache.double().numpy()
         out = bufs.out.float().cpu().numpy()
         lse = bufs.lse.cpu().numpy()
         done, fl, dO, dL = 0, 0.0, 0.0, 0.0
@@ -343,7 +356,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, help="1..8; 2 is the headline workload, 6 is 3 with an fp8 cache, 7-8 are GQA (MHA path)")
+    ap.add_argument("--workload", type=int, default=2, help="1..9; 2 is the headline workload, 6 is 3 with an fp8 cache, 7-9 are GQA (MHA path; 9 with fp8 K/V)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -111,6 +111,17 @@ typedef struct {
   void* out;                   /* device [batch, s_q, h_q, head_dim], dtype   */
   int64_t out_stride[3];       /*   strides of batch, token, head             */
   float* lse;                  /* device [batch, s_q, h_q] fp32, contiguous   */
+  /* Cache element type (mla_kv_dtype).  MLA_KV_SAME: both caches hold
+   * `dtype`.  MLA_KV_FP8_E4M3: both hold fp8 e4m3 codes (one byte each,
+   * strides still in elements) and the cached values are
+   *     K = code * k_scale[page * h_kv + g],  V = code * v_scale[page * h_kv + g]
+   * for physical page `page` and KV head g; requires dtype bf16 and every
+   * cache stride a multiple of 16.  Source: page "FlashMLA: 高性能GPU注意力机制
+   * 计算库 文件结构分析", section "项目主要功能" (FP8 KV cache); the scale
+   * granularity of one per page and KV head is this library's choice. */
+  int kv_dtype;
+  const float* k_scale;        /* device [num_pages, h_kv] fp32, finite; NULL means 1 */
+  const float* v_scale;        /* device [num_pages, h_kv] fp32, finite; NULL means 1 */
 } mha_decode_args;
 
 /*
@@ -123,6 +134,9 @@ typedef struct {
  * UNSUPPORTED (dtype, head_dim, page size), WORKSPACE_TOO_SMALL, HIP.
  */
 mla_status mha_decode(const mha_decode_args* args, void* stream);
+/* (also UNSUPPORTED: an fp8 cache with dtype other than bf16, or a kv_dtype
+ * this library does not know; INVALID_VALUE: an fp8 cache stride not a
+ * multiple of 16, a misaligned scale array) */
 
 /* First phase only: the split-KV kernel (whole units get their final out/lse,
  * pieces of split units go to the workspace).  Same arguments and errors. */

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 #define MLA_D_K 576             /* cached row width = query width           */
 #define MLA_D_V 512             /* value width: the first 512 columns       */

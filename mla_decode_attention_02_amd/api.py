@@ -90,6 +90,7 @@ class MhaArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64 * 3),
         ("lse", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -389,11 +390,22 @@ class MhaBuffers:
         self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
 
 
-def _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens):
+def _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens, k_scale=None, v_scale=None):
     if q.dtype not in DTYPE_CODES:
         raise ValueError("q must be bf16 or fp16")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("k_cache and v_cache must have q's dtype")
+    fp8 = k_cache.dtype == torch.float8_e4m3fn
+    if v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must have one dtype")
+    if k_cache.dtype != q.dtype and not (fp8 and q.dtype == torch.bfloat16):
+        raise ValueError("k_cache and v_cache must have q's dtype, or be float8_e4m3fn with a bf16 q")
+    for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if sc is None:
+            continue
+        if not fp8:
+            raise ValueError(f"{name} applies to fp8 caches only")
+        if sc.dtype != torch.float32 or sc.dim() != 2 or tuple(sc.shape) != (k_cache.shape[0], k_cache.shape[2]) \
+                or not sc.is_contiguous() or sc.device != q.device:
+            raise ValueError(f"{name} must be a contiguous fp32 [num_pages, h_kv] tensor on q's device")
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4 or block_table.dim() != 2 \
             or cache_seqlens.dim() != 1:
         raise ValueError("expected q [B,s_q,h_q,d], k_cache/v_cache [pages,64,h_kv,d], block_table [B,P], "
@@ -409,8 +421,9 @@ def _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens):
         raise ValueError("innermost dimensions must be contiguous")
 
 
-def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
-    _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens)
+def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+              k_scale=None, v_scale=None):
+    _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens, k_scale, v_scale)
     B, s_q, h_q, d = q.shape
     h_kv = k_cache.shape[2]
     if metadata is None:
@@ -440,6 +453,9 @@ def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_
     a.workspace_bytes = buffers.workspace.numel()
     a.out = buffers.out.data_ptr()
     a.lse = buffers.lse.data_ptr()
+    a.kv_dtype = 1 if k_cache.dtype == torch.float8_e4m3fn else 0
+    a.k_scale = k_scale.data_ptr() if k_scale is not None else None
+    a.v_scale = v_scale.data_ptr() if v_scale is not None else None
     _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
     return buffers.out, buffers.lse
 
@@ -447,24 +463,28 @@ def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_
 def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                cache_seqlens: torch.Tensor, softmax_scale: Optional[float] = None, causal: bool = False,
                metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-               buffers: Optional[MhaBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+               buffers: Optional[MhaBuffers] = None, k_scale: Optional[torch.Tensor] = None,
+               v_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MHA/GQA decode over separate K and V caches [pages, 64, h_kv, d]
     (d in 64, 128, 256; query head h reads KV head h // (h_q // h_kv)).
     Returns (out [B, s_q, h_q, d] in q's dtype, lse [B, s_q, h_q] fp32).
-    softmax_scale defaults to 1/sqrt(d)."""
+    softmax_scale defaults to 1/sqrt(d).  fp8 caches (torch.float8_e4m3fn, bf16
+    q) take optional fp32 scales k_scale / v_scale [num_pages, h_kv]."""
     if softmax_scale is None:
         softmax_scale = q.shape[-1] ** -0.5
     return _mha_call("mha_decode", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
-                     metadata, buffers)
+                     metadata, buffers, k_scale, v_scale)
 
 
-def mha_decode_splitkv(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+def mha_decode_splitkv(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+                       k_scale=None, v_scale=None):
     """First phase only (the MHA split-KV kernel)."""
     return _mha_call("mha_decode_splitkv", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
-                     metadata, buffers)
+                     metadata, buffers, k_scale, v_scale)
 
 
-def mha_decode_combine(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers):
+def mha_decode_combine(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
+                       k_scale=None, v_scale=None):
     """Second phase only (merge of split units)."""
     return _mha_call("mha_decode_combine", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
-                     metadata, buffers)
+                     metadata, buffers, k_scale, v_scale)

@@ -60,6 +60,16 @@ mla_status check_mha(const mha_decode_args* a) {
   if (!aligned(a->lse, 4) || !aligned(a->block_table, 4) || !aligned(a->cache_seqlens, 4) ||
       !aligned(a->sched, 4) || !aligned(a->split_offsets, 4))
     return fail(MLA_ERROR_INVALID_VALUE, "lse and the int32 arrays must be 4-byte aligned");
+  if (a->kv_dtype != MLA_KV_SAME && a->kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERROR_UNSUPPORTED, "kv_dtype %d is not 0 (same as dtype) or 1 (fp8 e4m3)", a->kv_dtype);
+  if (a->kv_dtype == MLA_KV_FP8_E4M3) {
+    if (a->dtype != MLA_DTYPE_BF16) return fail(MLA_ERROR_UNSUPPORTED, "an fp8 cache needs dtype bf16");
+    for (int i = 0; i < 3; ++i)
+      if (a->k_stride[i] % 16 || a->v_stride[i] % 16)
+        return fail(MLA_ERROR_INVALID_VALUE, "fp8 cache strides must be multiples of 16");
+    if (!aligned(a->k_scale, 4) || !aligned(a->v_scale, 4))
+      return fail(MLA_ERROR_INVALID_VALUE, "k_scale and v_scale must be 4-byte aligned");
+  }
   const int64_t* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->out_stride};
   const char* names[4] = {"q_stride", "k_stride", "v_stride", "out_stride"};
   for (int t = 0; t < 4; ++t)
@@ -113,6 +123,9 @@ mla::MhaParams make_mha_params(const mha_decode_args* a) {
   const size_t slots = (size_t)a->batch * a->h_kv + (size_t)a->num_parts;
   p.part_o = static_cast<float*>(a->workspace);
   p.part_lse = p.part_o + slots * (size_t)p.rows * a->head_dim;
+  p.kv_fp8 = a->kv_dtype == MLA_KV_FP8_E4M3;
+  p.k_scale = p.kv_fp8 ? a->k_scale : nullptr;
+  p.v_scale = p.kv_fp8 ? a->v_scale : nullptr;
   return p;
 }
 

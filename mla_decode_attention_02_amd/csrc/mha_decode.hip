@@ -23,6 +23,15 @@
 // Keys past a request's length in its last page are read over a range that
 // ends at its last valid row, so they arrive as zeros whatever the cache holds
 // there.
+//
+// fp8 caches (KV8): K and V hold e4m3 codes with one fp32 scale per page and
+// KV head.  The LDS image keeps the codes (half the bytes; eight buffers, seven
+// steps ahead) and operands are converted to bf16 as they are read (exact:
+// every e4m3 value is a bf16 value).  K operands are 16-byte reads whose 16
+// codes feed two MFMAs (the Q fragments are loaded in that column order); V^T
+// operands come from 8-bit transposed reads (eight keys of one column per
+// lane).  The K scale multiplies the scores, the V scale the probabilities
+// before their bf16 rounding (the denominator sums the unscaled ones).
 #include "mla_common.hpp"
 #include "mla_internal.h"
 
@@ -34,24 +43,45 @@ namespace mla {
 template <int CPR>
 __device__ __forceinline__ int mha_swz(int row) {
   if constexpr (CPR >= 16) return (row & 7) << 1;
-  else return ((row >> 1) & 3) << 1;
+  else if constexpr (CPR == 8) return ((row >> 1) & 3) << 1;
+  else return ((row >> 2) & 1) << 1;          // 64-byte rows, four per bank row
 }
 
-// Buffer descriptor over the rows of one page and KV head; rows at or past
-// `valid` are out of range (their loads return zeros).  valid <= 0: empty.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+__device__ __forceinline__ u32x2 mha_ld_tr8(const MLA_LDS char* p) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS v2i*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Buffer descriptor over the rows of one page and KV head (elements of ESZ
+// bytes); rows at or past `valid` are out of range (their loads return
+// zeros).  valid <= 0: empty.
+template <int ESZ>
 __device__ __forceinline__ BufRsrc mha_rows_rsrc(const void* base, int64_t elem_off, int64_t row_stride, int width,
                                                  int valid) {
-  const int bytes = valid > 0 ? (int)(((int64_t)(valid - 1) * row_stride + width) * 2) : 0;
-  return page_rsrc((const char*)base + elem_off * 2, bytes);
+  const int bytes = valid > 0 ? (int)(((int64_t)(valid - 1) * row_stride + width) * ESZ) : 0;
+  return page_rsrc((const char*)base + elem_off * ESZ, bytes);
 }
 
-template <typename T, int D, int RT>
+template <typename T, int D, int RT, bool KV8>
 __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   constexpr int DV = D;
   constexpr int KS = D <= 128 ? 64 : 32;     // keys per step
   constexpr int KT = KS / 16;                // 16-key score tiles per step
   constexpr int SPP = kPage / KS;            // steps per page
-  constexpr int ROWB = D * 2;                // bytes of a K (and V) row in LDS
+  constexpr int ESZ = KV8 ? 1 : 2;           // bytes per cached element
+  constexpr int NB = KV8 ? 8 : 4;            // LDS buffers (NB - 1 steps in flight)
+  constexpr int ROWB = D * ESZ;              // bytes of a K (and V) row in LDS
   constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
   constexpr int KBYTES = KS * ROWB;
   constexpr int BUF = 2 * KBYTES;            // K rows, then V rows
@@ -59,22 +89,50 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   constexpr int CW = DV / 4;                 // output columns per wave
   constexpr int CT = CW / 16;                // 16-column output tiles per wave
   constexpr int NDMA = 2 * KBYTES / 1024 / 4;  // LDS-DMA instructions per wave and step
+  constexpr int NLD = NDMA + (KV8 ? 2 : 0);  // and with the two scale loads
   constexpr int RPI = 1024 / ROWB;           // rows per DMA instruction
   static_assert(KT % 2 == 0 && CT >= 1 && NDMA >= 1 && 2 * KBYTES % 4096 == 0, "tile shape");
-  static_assert(3 * NDMA <= 63, "loads in flight fit the wait counter");
+  static_assert((NB - 1) * NLD <= 63, "loads in flight fit the wait counter");
   // K/V bytes are read once when the unit's rows fit one row block:
   // non-temporal; row blocks of one unit may meet in L2 otherwise
   constexpr int kAux = RT < 4 ? 2 : 0;
+  // one array per buffer, so that the compiler can tell the reads of one from
+  // the loads in flight into another
+  constexpr int BUFX = NB > 4 ? BUF : 16;
   __shared__ __attribute__((aligned(1024))) char b0_raw[BUF];
   __shared__ __attribute__((aligned(1024))) char b1_raw[BUF];
   __shared__ __attribute__((aligned(1024))) char b2_raw[BUF];
   __shared__ __attribute__((aligned(1024))) char b3_raw[BUF];
+  __shared__ __attribute__((aligned(1024))) char b4_raw[BUFX];
+  __shared__ __attribute__((aligned(1024))) char b5_raw[BUFX];
+  __shared__ __attribute__((aligned(1024))) char b6_raw[BUFX];
+  __shared__ __attribute__((aligned(1024))) char b7_raw[BUFX];
   auto buf = [&](auto ic) -> MLA_LDS char* {
-    constexpr int i = decltype(ic)::value & 3;
+    constexpr int i = decltype(ic)::value % NB;
     if constexpr (i == 0) return (MLA_LDS char*)b0_raw;
     else if constexpr (i == 1) return (MLA_LDS char*)b1_raw;
     else if constexpr (i == 2) return (MLA_LDS char*)b2_raw;
-    else return (MLA_LDS char*)b3_raw;
+    else if constexpr (i == 3) return (MLA_LDS char*)b3_raw;
+    else if constexpr (i == 4) return (MLA_LDS char*)b4_raw;
+    else if constexpr (i == 5) return (MLA_LDS char*)b5_raw;
+    else if constexpr (i == 6) return (MLA_LDS char*)b6_raw;
+    else return (MLA_LDS char*)b7_raw;
+  };
+  // fp8: the step's K and V scales, landed by LDS-DMA (each wave fills its own
+  // 64 floats, all read the first), one array per buffer
+  constexpr int SCX = KV8 ? 2 * 4 * 64 : 1;
+  __shared__ float s0_raw[SCX], s1_raw[SCX], s2_raw[SCX], s3_raw[SCX];
+  __shared__ float s4_raw[SCX], s5_raw[SCX], s6_raw[SCX], s7_raw[SCX];
+  auto sbuf = [&](auto ic) -> MLA_LDS float* {
+    constexpr int i = decltype(ic)::value % NB;
+    if constexpr (i == 0) return (MLA_LDS float*)s0_raw;
+    else if constexpr (i == 1) return (MLA_LDS float*)s1_raw;
+    else if constexpr (i == 2) return (MLA_LDS float*)s2_raw;
+    else if constexpr (i == 3) return (MLA_LDS float*)s3_raw;
+    else if constexpr (i == 4) return (MLA_LDS float*)s4_raw;
+    else if constexpr (i == 5) return (MLA_LDS float*)s5_raw;
+    else if constexpr (i == 6) return (MLA_LDS float*)s6_raw;
+    else return (MLA_LDS float*)s7_raw;
   };
 
   const int wave = wave_id();
@@ -105,7 +163,9 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
     bw.init(p.block_table + (int64_t)b * p.bt_s, lo, hi, lane);
 
     // Q fragments (B operand of S^T = K . Q^T): row rt*16 + li, columns
-    // ks*32 + 8g .. +8; rows past the unit's rows are zero
+    // ks*32 + 8g .. +8 (fp8: fragment 2m columns 64m + 16g .. +8 and 2m + 1
+    // the next 8, the order of the 16 codes one K read brings); rows past the
+    // unit's rows are zero
     u32x4 qf[RT][DC];
     int cnt[RT];
 #pragma unroll
@@ -116,7 +176,10 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         const int head = hk * p.group + (row - tok * p.group);
         const T* qp = (const T*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2 + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < DC; ++ks) qf[rt][ks] = *(const u32x4*)(qp + ks * 32);
+        for (int ks = 0; ks < DC; ++ks) {
+          const int col = KV8 ? 64 * (ks >> 1) + 8 * g + 8 * (ks & 1) : ks * 32;   // past qp's 8g
+          qf[rt][ks] = *(const u32x4*)(qp + col);
+        }
         cnt[rt] = visible_count(n, p.s_q, tok, p.causal);
       } else {
 #pragma unroll
@@ -138,8 +201,8 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       const int sub = kstep - page * SPP;
       const int phys = real ? bw.phys(page) : 0;
       const int valid = real ? min(kPage, n - page * kPage) : 0;
-      const BufRsrc kr = mha_rows_rsrc(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
-      const BufRsrc vr = mha_rows_rsrc(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, DV, valid);
+      const BufRsrc kr = mha_rows_rsrc<ESZ>(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
+      const BufRsrc vr = mha_rows_rsrc<ESZ>(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, DV, valid);
       int ln = lane;                             // opaque: offsets are rebuilt per step
       asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -151,8 +214,16 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         const int c = (ln % CPR) ^ mha_swz<CPR>(r);
         const int key = sub * KS + r;            // slot within the page
         const int64_t rs = isv ? p.v_s1 : p.k_s1;
-        const int voff = (int)(key * rs * 2) + c * 16;
+        const int voff = (int)(key * rs * ESZ) + c * 16;
         dma16<kAux>(isv ? vr : kr, bp + (isv ? KBYTES : 0) + jj * 1024, voff, 0);
+      }
+      if constexpr (KV8) {
+        MLA_LDS float* sp = sbuf(ic) + wave * 64;
+        const int soff = (phys * p.h_kv + hk) * 4;
+        const BufRsrc ks = page_rsrc((const char*)p.k_scale, p.k_scale && real ? 0x7FFFFFFF : 0);
+        const BufRsrc vs = page_rsrc((const char*)p.v_scale, p.v_scale && real ? 0x7FFFFFFF : 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, (MLA_LDS void*)sp, 4, 0, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vs, (MLA_LDS void*)(sp + 4 * 64), 4, 0, soff, 0, 0);
       }
     };
 
@@ -166,16 +237,19 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       for (int ct = 0; ct < CT; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    issue(std::integral_constant<int, 0>{}, 0);
-    issue(std::integral_constant<int, 1>{}, 1);
-    issue(std::integral_constant<int, 2>{}, 2);
+    static_for<0, NB - 1>([&](auto ic) { issue(ic, decltype(ic)::value); });
 
     auto step = [&](auto Hc, int s) {
       constexpr int H = decltype(Hc)::value;
-      dma_barrier<2 * NDMA>();                   // step s landed, everyone done with step s-1
-      issue(std::integral_constant<int, H + 3>{}, s + 3);
+      dma_barrier<(NB - 2) * NLD>();             // step s landed, everyone done with step s-1
+      issue(std::integral_constant<int, H + NB - 1>{}, s + NB - 1);
       MLA_LDS char* kb = buf(Hc);
       MLA_LDS char* vb = kb + KBYTES;
+      float kscl = 1.f, vscl = 1.f;              // fp8: this step's K and V scales
+      if constexpr (KV8) {
+        if (p.k_scale) kscl = sbuf(Hc)[0];
+        if (p.v_scale) vscl = sbuf(Hc)[4 * 64];
+      }
       // S^T tiles: keys kt*16 + 4g .. +4 of row li of tile rt
       f32x4 sc4[KT][RT];
 #pragma unroll
@@ -183,11 +257,25 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const MLA_LDS char* krow = kb + (kt * 16 + li) * ROWB;
+        if constexpr (KV8) {
 #pragma unroll
-        for (int ks = 0; ks < DC; ++ks) {
-          const u32x4 kf = ld_lds16(krow + (((ks * 4 + g) ^ ksw) << 4));
+          for (int m = 0; m < DC / 2; ++m) {
+            const u32x4 kw = ld_lds16(krow + (((m * 4 + g) ^ ksw) << 4));
+            const u32x4 ka = e4m3x8_to_bf16(kw[0], kw[1]);
+            const u32x4 kc = e4m3x8_to_bf16(kw[2], kw[3]);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = Dt<T>::mfma32(kf, qf[rt][ks], sc4[kt][rt]);
+            for (int rt = 0; rt < RT; ++rt) {
+              sc4[kt][rt] = Dt<T>::mfma32(ka, qf[rt][2 * m], sc4[kt][rt]);
+              sc4[kt][rt] = Dt<T>::mfma32(kc, qf[rt][2 * m + 1], sc4[kt][rt]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < DC; ++ks) {
+            const u32x4 kf = ld_lds16(krow + (((ks * 4 + g) ^ ksw) << 4));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = Dt<T>::mfma32(kf, qf[rt][ks], sc4[kt][rt]);
+          }
         }
       }
       // online softmax per row tile; probabilities packed as the B operand of
@@ -203,7 +291,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[kt][e] = (key0 + kt * 16 + e < cnt[rt]) ? sc4[kt][rt][e] : -INFINITY;
+            x[kt][e] = (key0 + kt * 16 + e < cnt[rt]) ? sc4[kt][rt][e] * kscl : -INFINITY;
             mx = fmaxf(mx, x[kt][e]);
           }
         mx = max_across_groups(mx) * p.scale_log2;   // scale > 0 commutes with the max
@@ -222,6 +310,12 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
             rs += x[kt][e];
           }
         l_part[rt] = l_part[rt] * alpha[rt] + rs;
+        if constexpr (KV8) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[kt][e] *= vscl;
+        }
 #pragma unroll
         for (int kp = 0; kp < KT / 2; ++kp)
           pf[rt][kp] = u32x4{Dt<T>::pack2(x[2 * kp][0], x[2 * kp][1]), Dt<T>::pack2(x[2 * kp][2], x[2 * kp][3]),
@@ -240,27 +334,46 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       // O^T += V^T . P^T for this wave's columns: transposed reads of value
       // rows 32kp + 4g + li/4 (lo) and +16 (hi), columns 4(li&3) .. +4 of the
       // 16-column tile
-      const int vr = 4 * g + (li >> 2);
-      const int vsw = mha_swz<CPR>(vr);          // the same for vr + 16, vr + 32
+      if constexpr (KV8) {
+        // lane 2r + h of group g addresses key slot r (keys 4g..4g+3, then
+        // 16+4g..16+4g+3 of the pair), column bytes 8h .. 8h+7 of the tile
+        const int vs = li >> 1;
+        const int vkey = vs < 4 ? 4 * g + vs : 12 + 4 * g + vs;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int chunk = (wave * CW + ct * 16) / 8 + ((li >> 1) & 1);
-        const int coff = ((chunk ^ vsw) << 4) + (li & 1) * 8;
+        for (int ct = 0; ct < CT; ++ct) {
+          const int chunk = (wave * CW + ct * 16) / 16;
 #pragma unroll
-        for (int kp = 0; kp < KT / 2; ++kp) {
-          const u32x2 lo4 = ld_lds_tr(vb + (32 * kp + vr) * ROWB + coff);
-          const u32x2 hi4 = ld_lds_tr(vb + (32 * kp + 16 + vr) * ROWB + coff);
-          const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+          for (int kp = 0; kp < KT / 2; ++kp) {
+            const int r = 32 * kp + vkey;
+            const u32x2 w = mha_ld_tr8(vb + r * ROWB + ((chunk ^ mha_swz<CPR>(r)) << 4) + (li & 1) * 8);
+            const u32x4 vf = e4m3x8_to_bf16(w[0], w[1]);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
+            for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
+          }
+        }
+      } else {
+        const int vr = 4 * g + (li >> 2);
+        const int vsw = mha_swz<CPR>(vr);          // the same for vr + 16, vr + 32
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int chunk = (wave * CW + ct * 16) / 8 + ((li >> 1) & 1);
+          const int coff = ((chunk ^ vsw) << 4) + (li & 1) * 8;
+#pragma unroll
+          for (int kp = 0; kp < KT / 2; ++kp) {
+            const u32x2 lo4 = ld_lds_tr(vb + (32 * kp + vr) * ROWB + coff);
+            const u32x2 hi4 = ld_lds_tr(vb + (32 * kp + 16 + vr) * ROWB + coff);
+            const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
+          }
         }
       }
     };
-    // whole groups of four steps, then the tail: every step of the loop body
+    // whole groups of NB steps, then the tail: every step of the loop body
     // runs, so the compiler sees which buffer each load in flight targets
     int s0 = 0;
-    for (; s0 + 4 <= nsteps; s0 += 4) static_for<0, 4>([&](auto Hc) { step(Hc, s0 + decltype(Hc)::value); });
-    static_for<0, 3>([&](auto Hc) {
+    for (; s0 + NB <= nsteps; s0 += NB) static_for<0, NB>([&](auto Hc) { step(Hc, s0 + decltype(Hc)::value); });
+    static_for<0, NB - 1>([&](auto Hc) {
       const int s = s0 + decltype(Hc)::value;
       if (s < nsteps) step(Hc, s);
     });
@@ -370,26 +483,26 @@ __global__ __launch_bounds__(256) void mha_combine_kernel(MhaParams p) {
 
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, bool KV8>
 hipError_t launch_mha_d(const MhaParams& p, hipStream_t st) {
   const int m_blocks = (p.rows + 63) / 64;
   const int rt = p.rows >= 64 ? 4 : (p.rows + 15) / 16;
   const dim3 grid(p.num_parts, m_blocks);
   switch (rt) {
-    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1>), grid, dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2>), grid, dim3(256), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3>), grid, dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4>), grid, dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1, KV8>), grid, dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2, KV8>), grid, dim3(256), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3, KV8>), grid, dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4, KV8>), grid, dim3(256), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool KV8>
 hipError_t launch_mha_t(const MhaParams& p, int head_dim, hipStream_t st) {
   switch (head_dim) {
-    case 64: return launch_mha_d<T, 64>(p, st);
-    case 128: return launch_mha_d<T, 128>(p, st);
-    case 256: return launch_mha_d<T, 256>(p, st);
+    case 64: return launch_mha_d<T, 64, KV8>(p, st);
+    case 128: return launch_mha_d<T, 128, KV8>(p, st);
+    case 256: return launch_mha_d<T, 256, KV8>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -409,7 +522,8 @@ hipError_t launch_mha_combine_t(const MhaParams& p, int head_dim, hipStream_t st
 }  // namespace
 
 hipError_t launch_mha_splitkv(const MhaParams& p, int dtype, int head_dim, hipStream_t st) {
-  return dtype == 0 ? launch_mha_t<__bf16>(p, head_dim, st) : launch_mha_t<_Float16>(p, head_dim, st);
+  if (p.kv_fp8) return launch_mha_t<__bf16, true>(p, head_dim, st);
+  return dtype == 0 ? launch_mha_t<__bf16, false>(p, head_dim, st) : launch_mha_t<_Float16, false>(p, head_dim, st);
 }
 
 hipError_t launch_mha_combine(const MhaParams& p, int dtype, int head_dim, hipStream_t st) {

@@ -86,6 +86,9 @@ struct MhaParams {
   float* lse;               // [batch, s_q, h_q]
   float* part_o;            // [slots, rows, d_v] fp32
   float* part_lse;          // [slots, rows]
+  int kv_fp8;               // caches hold fp8 e4m3 codes (bf16 q)
+  const float* k_scale;     // fp8: [num_pages, h_kv] scales of K (null: 1)
+  const float* v_scale;     // fp8: [num_pages, h_kv] scales of V (null: 1)
 };
 
 // Arguments of the merge of context-parallel shards (strides in elements).

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.mla_abi_version() == 3
+    assert L.mla_abi_version() == 4
     assert L.mla_last_error() is not None
 
 
@@ -278,6 +278,10 @@ MHA_BREAKS = [
     ("scale", lambda a: setattr(a, "softmax_scale", 0.0), INVALID),
     ("causal", lambda a: setattr(a, "causal", 5), INVALID),
     ("workspace small", lambda a: setattr(a, "workspace_bytes", 256), WS_SMALL),
+    ("kv_dtype", lambda a: setattr(a, "kv_dtype", 2), UNSUPPORTED),
+    ("fp8 with fp16", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "dtype", 1)), UNSUPPORTED),
+    ("fp8 stride", lambda a: (setattr(a, "kv_dtype", 1), a.k_stride.__setitem__(2, 136)), INVALID),
+    ("fp8 scale misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "v_scale", (1 << 24) + 2)), INVALID),
 ]
 
 

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import oracle_mha_decode, oracle_mha_metadata, oracle_mha_rows
+from oracle import dequantize_heads, oracle_mha_decode, oracle_mha_metadata, oracle_mha_rows
 from mla_decode_attention_02_amd import api
 from mla_decode_attention_02_amd.workloads import MHA_WORKLOADS, make_mha_inputs, mha_workload_inputs
 
@@ -41,9 +41,17 @@ def run(x, num_parts=None):
     h_kv = g.k_cache.shape[2]
     meta = api.mha_get_metadata(g.cache_seqlens, s_q, h_q, h_kv, num_parts=num_parts)
     out, lse = api.mha_decode(g.q, g.k_cache, g.v_cache, g.block_table, g.cache_seqlens, g.softmax_scale,
-                              g.causal, metadata=meta)
+                              g.causal, metadata=meta, k_scale=g.k_scale, v_scale=g.v_scale)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), [m.cpu().numpy() for m in meta]
+
+
+def kv64(x):
+    """K and V as the oracle sees them: exact float64 values (fp8 caches
+    through the oracle's own e4m3 decoder and per-page, per-head scales)."""
+    if x.k_cache.dtype == torch.float8_e4m3fn:
+        return dequantize_heads(x.k_cache, x.k_scale), dequantize_heads(x.v_cache, x.v_scale)
+    return x.k_cache.double().numpy(), x.v_cache.double().numpy()
 
 
 def compare(out, lse, ref_o, ref_l, tag):
@@ -182,8 +190,81 @@ def test_mha_workload_full_size_sampled(idx):
     out, lse, meta = run(x)
     seqlens = x.cache_seqlens.tolist()
     picks = sorted(set([0, w.batch - 1, int(np.argmax(seqlens))]))
-    qf, kf, vf = x.q.double().numpy(), x.k_cache.double().numpy(), x.v_cache.double().numpy()
+    qf = x.q.double().numpy()
+    kf, vf = kv64(x)
     for b in picks:
         ref_o, ref_l = oracle_mha_rows(qf, kf, vf, x.block_table, x.cache_seqlens, x.softmax_scale, w.causal, b)
         compare(out[b], lse[b], ref_o, ref_l, f"mha workload {idx} request {b}")
     assert np.isfinite(lse).all()
+
+
+FP8_EDGE = [
+    # (s_q, h_q, h_kv, d, seqlens, causal, scale_mode, num_parts)
+    (1, 8, 2, 128, (1, 2, 63, 64, 65), False, "amax", None),
+    (1, 8, 8, 128, (127, 128, 129, 1000), False, "pow2", 3),
+    (2, 16, 2, 128, (1, 2, 65, 300), True, "amax", 2),
+    (1, 4, 1, 64, (5, 300, 64), False, "none", 1),
+    (3, 6, 3, 64, (300, 7, 64), True, "amax", 5),
+    (1, 32, 4, 256, (33, 64, 65, 500), False, "amax", None),
+    (2, 8, 4, 256, (1, 31, 32, 33, 97), True, "pow2", 4),
+    (1, 64, 1, 128, (200, 1000), False, "amax", 6),        # 64 rows: one full row block
+    (2, 40, 2, 128, (2, 129, 300), True, "amax", 3),       # 40 rows: three row tiles
+    (1, 12, 4, 128, (5000,), False, "amax", 17),           # one long request cut into many pieces
+]
+
+
+@pytest.mark.parametrize("s_q,h_q,h_kv,d,seqlens,causal,mode,parts", FP8_EDGE,
+                         ids=[f"sq{c[0]}_hq{c[1]}_hkv{c[2]}_d{c[3]}_{'c' if c[5] else 'n'}_{c[6]}_p{c[7]}"
+                              for c in FP8_EDGE])
+def test_mha_fp8_parity(s_q, h_q, h_kv, d, seqlens, causal, mode, parts):
+    """fp8 e4m3 K/V caches with one scale per page and KV head (or none),
+    against the oracle on the dequantised caches."""
+    tag = f"mha fp8 s_q={s_q} h_q={h_q} h_kv={h_kv} d={d} seqlens={seqlens} causal={causal} {mode} parts={parts}"
+    _say(tag)
+    x = make_mha_inputs(len(seqlens), s_q, h_q, h_kv, d, "bf16", seqlens=seqlens, causal=causal,
+                        seed=sum(seqlens) + 3 * h_q + d, poison=True, extra_pages=2, kv_dtype="fp8",
+                        scale_mode=mode)
+    out, lse, _ = run(x, parts)
+    kf, vf = kv64(x)
+    ref_o, ref_l = oracle_mha_decode(x.q, kf, vf, x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+    compare(out, lse, ref_o, ref_l, tag)
+
+
+def test_mha_fp8_scales_reach_both_caches():
+    """Doubling every V scale doubles O; halving every K scale and doubling
+    softmax_scale changes nothing (both exact in fp32, so bit for bit)."""
+    _say("mha fp8 scale propagation")
+    x = make_mha_inputs(3, 1, 16, 4, 128, "bf16", seqlens=(70, 500, 9), seed=31, kv_dtype="fp8")
+    out1, lse1, _ = run(x, 3)
+    x2 = make_mha_inputs(3, 1, 16, 4, 128, "bf16", seqlens=(70, 500, 9), seed=31, kv_dtype="fp8")
+    x2.v_scale = x2.v_scale * 2
+    out2, lse2, _ = run(x2, 3)
+    assert np.array_equal(lse1, lse2) and np.array_equal(out2, 2 * out1)
+    x3 = make_mha_inputs(3, 1, 16, 4, 128, "bf16", seqlens=(70, 500, 9), seed=31, kv_dtype="fp8")
+    x3.k_scale = x3.k_scale * 0.5
+    x3.softmax_scale = x.softmax_scale * 2
+    out3, lse3, _ = run(x3, 3)
+    assert np.array_equal(out1, out3) and np.array_equal(lse1, lse3)
+
+
+def test_mha_fp8_nan_codes_in_unused_slots_and_pages():
+    """NaN codes past a request's length and in unused pages, and NaN scales
+    of unused pages, change nothing: those bytes are never used."""
+    _say("mha fp8 NaN codes in unused slots and pages")
+    seqlens = (70, 130, 3)
+    x = make_mha_inputs(3, 1, 8, 2, 128, "bf16", seqlens=seqlens, seed=29, extra_pages=3, kv_dtype="fp8")
+    out1, lse1, _ = run(x, 4)
+    nan8 = torch.full((1,), 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    for b, n in enumerate(seqlens):
+        page = int(x.block_table[b, (n + 63) // 64 - 1])
+        x.k_cache[page, n % 64:] = nan8
+        x.v_cache[page, n % 64:] = nan8
+    used = set(int(v) for v in x.block_table.flatten().tolist() if v >= 0)
+    for page in range(x.k_cache.shape[0]):
+        if page not in used:
+            x.k_cache[page] = nan8
+            x.v_cache[page] = nan8
+            x.k_scale[page] = float("nan")
+            x.v_scale[page] = float("inf")
+    out2, lse2, _ = run(x, 4)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
