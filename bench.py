@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "splitkv_narrow_kernel": ["mla_splitkv_narrow.hip", "mla_splitkv.hpp", "mla_common.hpp"],
     "splitkv_fp8_kernel": ["mla_splitkv_fp8.hip", "mla_splitkv.hpp", "mla_common.hpp"],
     "mha_splitkv_kernel": ["mha_decode.hip", "mla_common.hpp"],
+    "mha_keysplit_kernel": ["mha_decode.hip", "mla_common.hpp"],
 }
 
 
@@ -53,6 +54,17 @@ def mla_kernel_name(w) -> str:
     if w.kv == "fp8":
         return "splitkv_fp8_kernel"
     return "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
+
+
+def mha_kernel_name(w) -> str:
+    """The MHA split-KV kernel that runs a workload: the key-split one while
+    a block's row tiles times the head size stay within 256 (bf16 caches up to
+    d = 128), else the column-split one."""
+    rows = w.s_q * (w.h_q // w.h_kv)
+    rt = 4 if rows >= 64 else (rows + 15) // 16
+    if rt * w.head_dim <= 256 and (w.kv == "fp8" or w.head_dim <= 128):
+        return "mha_keysplit_kernel"
+    return "mha_splitkv_kernel"
 COPY_MIB = 1024
 
 
@@ -97,7 +109,7 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
 
     mha = workload in MHA_WORKLOADS
     w = MHA_WORKLOADS[workload] if mha else WORKLOADS[workload]
-    kernel = "mha_splitkv_kernel" if mha else mla_kernel_name(w)
+    kernel = mha_kernel_name(w) if mha else mla_kernel_name(w)
     tag = f"w{workload}"
     stats = _counter_rows(os.path.join(out_dir, f"prof_{tag}", f"{tag}_kernel_stats.csv"))
 
@@ -258,8 +270,8 @@ def bench_mha(args) -> dict:
     kavg = sum(ks) / len(ks)
     ach = splitkv_bytes / (kavg * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": stored_traffic("mha_splitkv_kernel", w.name),
-            "kernel": "mha_splitkv_kernel", "kernel_avg_us": round(kavg * 1e3, 2),
+            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(mha_kernel_name(w), w.name),
+            "kernel": mha_kernel_name(w), "kernel_avg_us": round(kavg * 1e3, 2),
             "kernel_p10_p90_us": [round(ks[len(ks) // 10] * 1e3, 2), round(ks[(9 * len(ks)) // 10] * 1e3, 2)],
             "algorithmic_bytes_per_launch": splitkv_bytes, "algorithmic_flops_per_launch": flops}
     result = {

@@ -97,12 +97,15 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   // non-temporal; row blocks of one unit may meet in L2 otherwise
   constexpr int kAux = RT < 4 ? 2 : 0;
   // one array per buffer, so that the compiler can tell the reads of one from
-  // the loads in flight into another
-  constexpr int BUFX = NB > 4 ? BUF : 16;
-  __shared__ __attribute__((aligned(1024))) char b0_raw[BUF];
-  __shared__ __attribute__((aligned(1024))) char b1_raw[BUF];
-  __shared__ __attribute__((aligned(1024))) char b2_raw[BUF];
-  __shared__ __attribute__((aligned(1024))) char b3_raw[BUF];
+  // the loads in flight into another (it tells apart at most eight LDS-DMA
+  // targets, so the fp8 scales live at the end of their buffer's array)
+  constexpr int SCB = KV8 ? 2 * 4 * 64 * 4 : 0;   // fp8: K and V scale slots, 64 floats per wave
+  constexpr int BUFA = BUF + SCB;
+  constexpr int BUFX = NB > 4 ? BUFA : 16;
+  __shared__ __attribute__((aligned(1024))) char b0_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b1_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b2_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b3_raw[BUFA];
   __shared__ __attribute__((aligned(1024))) char b4_raw[BUFX];
   __shared__ __attribute__((aligned(1024))) char b5_raw[BUFX];
   __shared__ __attribute__((aligned(1024))) char b6_raw[BUFX];
@@ -119,21 +122,8 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
     else return (MLA_LDS char*)b7_raw;
   };
   // fp8: the step's K and V scales, landed by LDS-DMA (each wave fills its own
-  // 64 floats, all read the first), one array per buffer
-  constexpr int SCX = KV8 ? 2 * 4 * 64 : 1;
-  __shared__ float s0_raw[SCX], s1_raw[SCX], s2_raw[SCX], s3_raw[SCX];
-  __shared__ float s4_raw[SCX], s5_raw[SCX], s6_raw[SCX], s7_raw[SCX];
-  auto sbuf = [&](auto ic) -> MLA_LDS float* {
-    constexpr int i = decltype(ic)::value % NB;
-    if constexpr (i == 0) return (MLA_LDS float*)s0_raw;
-    else if constexpr (i == 1) return (MLA_LDS float*)s1_raw;
-    else if constexpr (i == 2) return (MLA_LDS float*)s2_raw;
-    else if constexpr (i == 3) return (MLA_LDS float*)s3_raw;
-    else if constexpr (i == 4) return (MLA_LDS float*)s4_raw;
-    else if constexpr (i == 5) return (MLA_LDS float*)s5_raw;
-    else if constexpr (i == 6) return (MLA_LDS float*)s6_raw;
-    else return (MLA_LDS float*)s7_raw;
-  };
+  // 64 floats, all read the first)
+  auto sbuf = [&](auto ic) -> MLA_LDS float* { return (MLA_LDS float*)(buf(ic) + BUF); };
 
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
@@ -345,7 +335,10 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
 #pragma unroll
           for (int kp = 0; kp < KT / 2; ++kp) {
             const int r = 32 * kp + vkey;
-            const u32x2 w = mha_ld_tr8(vb + r * ROWB + ((chunk ^ mha_swz<CPR>(r)) << 4) + (li & 1) * 8);
+            // the offset masked to the V half, so the compiler can see that the
+            // read stays inside this buffer (else it waits for every load in flight)
+            const int off = (r * ROWB + ((chunk ^ mha_swz<CPR>(r)) << 4) + (li & 1) * 8) & (KBYTES - 1);
+            const u32x2 w = mha_ld_tr8(vb + off);
             const u32x4 vf = e4m3x8_to_bf16(w[0], w[1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
@@ -406,6 +399,368 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         if (wave == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
       }
     }
+  }
+}
+
+// ----------------------------------------------------------- key split --
+// Variant for few query rows per unit (row tiles RT with RT * d <= 256): the
+// four waves split each step's 64 keys instead of the output columns.  Wave w
+// scores keys 16w .. 16w+15 of the step for all of the block's rows, runs its
+// own online softmax over them and accumulates all d output columns from its
+// own keys (16x16x16 MFMAs, the P^T operand straight from the score
+// registers); the four partial states merge once per chunk through LDS.  Per
+// step and wave this is a quarter of the score MFMAs, operand reads, fp8
+// conversions and softmax arithmetic of the column-split kernel above, which
+// repeats all of them in every wave; at one wave per SIMD that instruction
+// stream, not HBM, bounds the column-split kernel for small groups.
+// The staging of K and V (LDS-DMA, buffers named at compile time, steps in
+// flight, fp8 scales) is that of the kernel above.
+template <typename T, int D, int RT, bool KV8>
+__global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
+  constexpr int KS = 64;                     // keys per step (one page), 16 per wave
+  constexpr int ESZ = KV8 ? 1 : 2;
+  constexpr int ROWB = D * ESZ;
+  constexpr int CPR = ROWB / 16;
+  constexpr int KBYTES = KS * ROWB;
+  constexpr int BUF = 2 * KBYTES;
+  constexpr int SCB = KV8 ? 2 * 4 * 64 * 4 : 0;
+  constexpr int MRG = RT * D * 64;           // one wave's partial O in the merge
+  constexpr int BUFA = BUF + SCB > MRG ? BUF + SCB : MRG;
+  constexpr int NB = 8 * BUFA <= 150 * 1024 ? 8 : 4;
+  constexpr int DC = D / 32;
+  constexpr int NCT = D / 16;                // 16-column output tiles (all of them, per wave)
+  constexpr int MCT = NCT / 4;               // tiles each wave merges
+  constexpr int NDMA = 2 * KBYTES / 1024 / 4;
+  constexpr int NLD = NDMA + (KV8 ? 2 : 0);
+  constexpr int RPI = 1024 / ROWB;
+  static_assert(RT * D <= 256 && MCT >= 1 && NDMA >= 1 && 2 * KBYTES % 4096 == 0, "tile shape");
+  static_assert((NB - 1) * NLD <= 63, "loads in flight fit the wait counter");
+  static_assert(NB * BUFA <= 160 * 1024 - 2 * 4 * 64 * 4, "LDS");
+  constexpr int kAux = 2;                    // rows fit one row block: K/V read once, non-temporal
+  constexpr int BUFX = NB > 4 ? BUFA : 16;
+  __shared__ __attribute__((aligned(1024))) char b0_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b1_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b2_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b3_raw[BUFA];
+  __shared__ __attribute__((aligned(1024))) char b4_raw[BUFX];
+  __shared__ __attribute__((aligned(1024))) char b5_raw[BUFX];
+  __shared__ __attribute__((aligned(1024))) char b6_raw[BUFX];
+  __shared__ __attribute__((aligned(1024))) char b7_raw[BUFX];
+  __shared__ float ml_s[2][4][64];           // merge: each wave's row maxima and sums
+  auto buf = [&](auto ic) -> MLA_LDS char* {
+    constexpr int i = decltype(ic)::value % NB;
+    if constexpr (i == 0) return (MLA_LDS char*)b0_raw;
+    else if constexpr (i == 1) return (MLA_LDS char*)b1_raw;
+    else if constexpr (i == 2) return (MLA_LDS char*)b2_raw;
+    else if constexpr (i == 3) return (MLA_LDS char*)b3_raw;
+    else if constexpr (i == 4) return (MLA_LDS char*)b4_raw;
+    else if constexpr (i == 5) return (MLA_LDS char*)b5_raw;
+    else if constexpr (i == 6) return (MLA_LDS char*)b6_raw;
+    else return (MLA_LDS char*)b7_raw;
+  };
+  auto sbuf = [&](auto ic) -> MLA_LDS float* { return (MLA_LDS float*)(buf(ic) + BUF); };
+
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int mrow0 = blockIdx.y * 64;
+  const int krow = 16 * wave + li;           // K row of the step this lane feeds to the score MFMAs
+  const int ksw = mha_swz<CPR>(krow);
+
+  const int32_t* sc = p.sched + blockIdx.x * 8;
+  const int begin_u = ldu(sc + 0), begin_page = ldu(sc + 1);
+  const int end_u = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
+  for (int u = begin_u; u <= end_u; ++u) {
+    const int b = u / p.h_kv;
+    const int hk = u - b * p.h_kv;
+    const int n = ldu(p.seqlens + b);
+    const int npages = (n + kPage - 1) / kPage;
+    const int lo = (u == begin_u) ? begin_page : 0;
+    const int hi = (u == end_u) ? end_page : npages;
+    if (lo >= hi) continue;
+    const int split = (u == begin_u) ? begin_split : 0;
+    const int slot0 = ldu(p.split_offsets + u);
+    const int nsplit = ldu(p.split_offsets + u + 1) - slot0;
+    const int nsteps = hi - lo;              // one step per page
+
+    BlockWindow bw;
+    bw.init(p.block_table + (int64_t)b * p.bt_s, lo, hi, lane);
+
+    // Q fragments: the B operand of S^T = K . Q^T, as in the kernel above
+    u32x4 qf[RT][DC];
+    int cnt[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = mrow0 + rt * 16 + li;
+      if (row < p.rows) {
+        const int tok = row / p.group;
+        const int head = hk * p.group + (row - tok * p.group);
+        const T* qp = (const T*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2 + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) {
+          const int col = KV8 ? 64 * (ks >> 1) + 8 * g + 8 * (ks & 1) : ks * 32;   // past qp's 8g
+          qf[rt][ks] = *(const u32x4*)(qp + col);
+        }
+        cnt[rt] = visible_count(n, p.s_q, tok, p.causal);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) qf[rt][ks] = u32x4{0, 0, 0, 0};
+        cnt[rt] = 0;
+      }
+    }
+
+    // LDS-DMA loads of page lo + s into buffer ic (every wave moves NDMA KiB
+    // of the K then V rows; lane l fills slot l of its KiB, i.e. row
+    // j*RPI + l / CPR, chunk (l % CPR) ^ swizzle(row)); steps past the chunk
+    // use empty descriptors, so every step issues the same loads.
+    auto issue = [&](auto ic, int s) {
+      MLA_LDS char* bp = buf(ic);
+      const bool real = s < nsteps;
+      const int page = lo + s;
+      const int phys = real ? bw.phys(page) : 0;
+      const int valid = real ? min(kPage, n - page * kPage) : 0;
+      const BufRsrc kr = mha_rows_rsrc<ESZ>(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
+      const BufRsrc vr = mha_rows_rsrc<ESZ>(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, D, valid);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int j = wave * NDMA + i;
+        const bool isv = j >= KBYTES / 1024;
+        const int jj = isv ? j - KBYTES / 1024 : j;
+        const int r = jj * RPI + ln / CPR;
+        const int c = (ln % CPR) ^ mha_swz<CPR>(r);
+        const int64_t rs = isv ? p.v_s1 : p.k_s1;
+        const int voff = (int)(r * rs * ESZ) + c * 16;
+        dma16<kAux>(isv ? vr : kr, bp + (isv ? KBYTES : 0) + jj * 1024, voff, 0);
+      }
+      if constexpr (KV8) {
+        MLA_LDS float* sp = sbuf(ic) + wave * 64;
+        const int soff = (phys * p.h_kv + hk) * 4;
+        const BufRsrc ksr = page_rsrc((const char*)p.k_scale, p.k_scale && real ? 0x7FFFFFFF : 0);
+        const BufRsrc vsr = page_rsrc((const char*)p.v_scale, p.v_scale && real ? 0x7FFFFFFF : 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ksr, (MLA_LDS void*)sp, 4, 0, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vsr, (MLA_LDS void*)(sp + 4 * 64), 4, 0, soff, 0, 0);
+      }
+    };
+
+    float m_run[RT], l_part[RT];
+    f32x4 o[RT][NCT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      m_run[rt] = -INFINITY;
+      l_part[rt] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    static_for<0, NB - 1>([&](auto ic) { issue(ic, decltype(ic)::value); });
+
+    auto step = [&](auto Hc, int s) {
+      constexpr int H = decltype(Hc)::value;
+      dma_barrier<(NB - 2) * NLD>();             // step s landed, everyone done with step s-1
+      issue(std::integral_constant<int, H + NB - 1>{}, s + NB - 1);
+      MLA_LDS char* kb = buf(Hc);
+      MLA_LDS char* vb = kb + KBYTES;
+      // operand reads first (with one wave per SIMD nothing else hides their
+      // latency): the K rows of this wave's keys, then the V^T tiles
+      const MLA_LDS char* kp = kb + krow * ROWB;
+      u32x4 kf[KV8 ? DC / 2 : DC];
+#pragma unroll
+      for (int m = 0; m < (KV8 ? DC / 2 : DC); ++m) kf[m] = ld_lds16(kp + (((m * 4 + g) ^ ksw) << 4));
+      // V^T: bf16 - lane (li, g) addresses key 16w + 4g + li/4, columns
+      // 16ct + 4(li&3) .. +4 and receives column li of keys 16w+4g .. +4;
+      // fp8 - lane 2r + h addresses key 16w + 4g + (r&3), bytes 8h..8h+7 of
+      // tile 2cp + r/4, and receives column li of those four keys in tiles
+      // 2cp and 2cp + 1
+      constexpr int NVR = KV8 ? NCT / 2 : NCT;
+      u32x2 vw[NVR];
+      if constexpr (KV8) {
+        const int vrow = 16 * wave + 4 * g + ((li >> 1) & 3);
+        const int vsw = mha_swz<CPR>(vrow);
+#pragma unroll
+        for (int cp = 0; cp < NVR; ++cp) {
+          const int chunk = 2 * cp + (li >> 3);
+          const int off = (vrow * ROWB + ((chunk ^ vsw) << 4) + (li & 1) * 8) & (KBYTES - 1);
+          vw[cp] = mha_ld_tr8(vb + off);
+        }
+      } else {
+        const int vrow = 16 * wave + 4 * g + (li >> 2);
+        const int vsw = mha_swz<CPR>(vrow);
+#pragma unroll
+        for (int ct = 0; ct < NVR; ++ct) {
+          const int chunk = 2 * ct + ((li >> 1) & 1);
+          const int off = (vrow * ROWB + ((chunk ^ vsw) << 4) + (li & 1) * 8) & (KBYTES - 1);
+          vw[ct] = ld_lds_tr(vb + off);
+        }
+      }
+      float kscl = 1.f, vscl = 1.f;
+      if constexpr (KV8) {
+        if (p.k_scale) kscl = sbuf(Hc)[0];
+        if (p.v_scale) vscl = sbuf(Hc)[4 * 64];
+      }
+      // S^T: keys 16w + 4g .. +4 (of the step) of row li of tile rt
+      f32x4 sc4[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) sc4[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KV8) {
+#pragma unroll
+        for (int m = 0; m < DC / 2; ++m) {
+          const u32x4 ka = e4m3x8_to_bf16(kf[m][0], kf[m][1]);
+          const u32x4 kc = e4m3x8_to_bf16(kf[m][2], kf[m][3]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            sc4[rt] = Dt<T>::mfma32(ka, qf[rt][2 * m], sc4[rt]);
+            sc4[rt] = Dt<T>::mfma32(kc, qf[rt][2 * m + 1], sc4[rt]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) sc4[rt] = Dt<T>::mfma32(kf[ks], qf[rt][ks], sc4[rt]);
+      }
+      // online softmax over this wave's keys; P^T operand = the lane's four
+      // probabilities (keys 4g .. 4g+3 of the wave's 16, row li)
+      u32x2 pf[RT];
+      float alpha[RT];
+      const int key0 = (lo + s) * KS + 16 * wave + 4 * g;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = (key0 + e < cnt[rt]) ? sc4[rt][e] * kscl : -INFINITY;
+          mx = fmaxf(mx, x[e]);
+        }
+        mx = max_across_groups(mx) * p.scale_log2;
+        alpha[rt] = 1.f;
+        if (mx > m_run[rt] + kRescaleSlack) {
+          alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - mx);
+          m_run[rt] = mx;
+        }
+        const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], p.scale_log2, -msub));
+          rs += x[e];
+        }
+        l_part[rt] = l_part[rt] * alpha[rt] + rs;
+        if constexpr (KV8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] *= vscl;
+        }
+        pf[rt] = u32x2{Dt<T>::pack2(x[0], x[1]), Dt<T>::pack2(x[2], x[3])};
+      }
+      bool resc = false;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) resc |= alpha[rt] != 1.f;
+      if (__any(resc)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) o[rt][ct] *= alpha[rt];
+      }
+      // O^T += V^T . P^T over the wave's 16 keys, every column tile
+      if constexpr (KV8) {
+#pragma unroll
+        for (int cp = 0; cp < NVR; ++cp) {
+          const u32x4 vf = e4m3x8_to_bf16(vw[cp][0], vw[cp][1]);
+          const u32x2 va = u32x2{vf[0], vf[1]}, vc = u32x2{vf[2], vf[3]};
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            o[rt][2 * cp] = Dt<T>::mfma16(va, pf[rt], o[rt][2 * cp]);
+            o[rt][2 * cp + 1] = Dt<T>::mfma16(vc, pf[rt], o[rt][2 * cp + 1]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma16(vw[ct], pf[rt], o[rt][ct]);
+      }
+    };
+    int s0 = 0;
+    for (; s0 + NB <= nsteps; s0 += NB) static_for<0, NB>([&](auto Hc) { step(Hc, s0 + decltype(Hc)::value); });
+    static_for<0, NB - 1>([&](auto Hc) {
+      const int s = s0 + decltype(Hc)::value;
+      if (s < nsteps) step(Hc, s);
+    });
+    // drain the loads issued past the end; after this barrier no wave reads
+    // the buffers, which now take the partial states
+    dma_barrier<0>();
+
+    // merge of the four waves' states: wave w's O tiles go to buffer w as
+    // [rt][ct][lane] (16 bytes per lane), its row maxima and sums to ml_s
+    {
+      MLA_LDS char* mine = wave == 0 ? buf(std::integral_constant<int, 0>{})
+                         : wave == 1 ? buf(std::integral_constant<int, 1>{})
+                         : wave == 2 ? buf(std::integral_constant<int, 2>{})
+                                     : buf(std::integral_constant<int, 3>{});
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float l = sum_across_groups(l_part[rt]);
+        if (g == 0) {
+          ml_s[0][wave][rt * 16 + li] = m_run[rt];
+          ml_s[1][wave][rt * 16 + li] = l;
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) *(MLA_LDS f32x4*)(mine + ((rt * NCT + ct) * 64 + lane) * 16) = o[rt][ct];
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = mrow0 + rt * 16 + li;
+      float mw[4], M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mw[w] = ml_s[0][w][rt * 16 + li];
+        M = fmaxf(M, mw[w]);
+      }
+      float sw[4], L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        sw[w] = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        L += sw[w] * ml_s[1][w][rt * 16 + li];
+      }
+      if (row >= p.rows) continue;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      const int tok = row / p.group;
+      const int head = hk * p.group + (row - tok * p.group);
+      f32x4 acc[MCT];
+#pragma unroll
+      for (int j = 0; j < MCT; ++j) {
+        const int ct = wave * MCT + j;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        static_for<0, 4>([&](auto wc) {
+          constexpr int w = decltype(wc)::value;
+          const f32x4 v = *(const MLA_LDS f32x4*)(buf(wc) + ((rt * NCT + ct) * 64 + lane) * 16);
+          acc[j] += v * sw[w];
+        });
+        acc[j] *= inv;
+      }
+      if (nsplit == 1) {
+        T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + 4 * g;
+#pragma unroll
+        for (int j = 0; j < MCT; ++j)
+          *(u32x2*)(dst + (wave * MCT + j) * 16) = u32x2{Dt<T>::pack2(acc[j][0], acc[j][1]),
+                                                         Dt<T>::pack2(acc[j][2], acc[j][3])};
+        if (wave == 0 && g == 0) p.lse[((int64_t)b * p.s_q + tok) * p.h_q + head] = lse;
+      } else {
+        const int64_t slot = slot0 + split;
+        float* dst = p.part_o + (slot * p.rows + row) * D + 4 * g;
+#pragma unroll
+        for (int j = 0; j < MCT; ++j) *(f32x4*)(dst + (wave * MCT + j) * 16) = acc[j];
+        if (wave == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+      }
+    }
+    // the buffers are refilled by the next chunk's loads: everyone must be
+    // done reading the partial states first
+    lds_barrier();
   }
 }
 
@@ -483,11 +838,30 @@ __global__ __launch_bounds__(256) void mha_combine_kernel(MhaParams p) {
 
 namespace {
 
+// Key-split kernel where its per-wave state fits (RT * d <= 256) and its
+// buffers leave loads in flight (bf16 caches up to d = 128)
+template <typename T, int D, bool KV8, int RT>
+constexpr bool kKeySplit = RT * D <= 256 && (KV8 || D <= 128);
+
+template <typename T, int D, bool KV8, int RT>
+bool launch_keysplit(int rt, dim3 grid, const MhaParams& p, hipStream_t st) {
+  if constexpr (kKeySplit<T, D, KV8, RT>) {
+    if (rt == RT) {
+      hipLaunchKernelGGL((mha_keysplit_kernel<T, D, RT, KV8>), grid, dim3(256), 0, st, p);
+      return true;
+    }
+  }
+  return false;
+}
+
 template <typename T, int D, bool KV8>
 hipError_t launch_mha_d(const MhaParams& p, hipStream_t st) {
   const int m_blocks = (p.rows + 63) / 64;
   const int rt = p.rows >= 64 ? 4 : (p.rows + 15) / 16;
   const dim3 grid(p.num_parts, m_blocks);
+  if (launch_keysplit<T, D, KV8, 1>(rt, grid, p, st) || launch_keysplit<T, D, KV8, 2>(rt, grid, p, st) ||
+      launch_keysplit<T, D, KV8, 3>(rt, grid, p, st) || launch_keysplit<T, D, KV8, 4>(rt, grid, p, st))
+    return hipGetLastError();
   switch (rt) {
     case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1, KV8>), grid, dim3(256), 0, st, p); break;
     case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2, KV8>), grid, dim3(256), 0, st, p); break;
