@@ -57,12 +57,12 @@ def mla_kernel_name(w) -> str:
 
 
 def mha_kernel_name(w) -> str:
-    """The MHA split-KV kernel that runs a workload: the key-split one while
-    a block's row tiles times the head size stay within 256 (bf16 caches up to
-    d = 128), else the column-split one."""
+    """The MHA split-KV kernel that runs a workload: the key-split one for an
+    fp8 cache while a block's row tiles times the head size stay within 256,
+    else the column-split one."""
     rows = w.s_q * (w.h_q // w.h_kv)
     rt = 4 if rows >= 64 else (rows + 15) // 16
-    if rt * w.head_dim <= 256 and (w.kv == "fp8" or w.head_dim <= 128):
+    if rt * w.head_dim <= 256 and w.kv == "fp8":
         return "mha_keysplit_kernel"
     return "mha_splitkv_kernel"
 COPY_MIB = 1024
