@@ -107,3 +107,22 @@ def test_mha_graph_replay():
         return api.mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, metadata=m, buffers=gbufs)
 
     _replays_match(run, eager)
+
+
+def test_mha_fp8_graph_replay():
+    _say("graph replay MHA, fp8 K/V caches")
+    x = make_mha_inputs(3, 1, 16, 4, 128, "bf16", seqlens=(1500, 64, 7), seed=64,
+                        kv_dtype="fp8").to(torch.device("cuda:0"))
+    meta = api.mha_get_metadata(x.cache_seqlens, 1, 16, 4, num_parts=11)
+    o, l = api.mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, metadata=meta,
+                          k_scale=x.k_scale, v_scale=x.v_scale)
+    torch.cuda.synchronize()
+    eager = (o.clone(), l.clone())
+    gbufs = api.MhaBuffers(x.q, 4, 11)
+
+    def run():
+        m = api.mha_get_metadata(x.cache_seqlens, 1, 16, 4, num_parts=11)
+        return api.mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, metadata=m, buffers=gbufs,
+                              k_scale=x.k_scale, v_scale=x.v_scale)
+
+    _replays_match(run, eager)

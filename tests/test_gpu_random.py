@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import dequantize_cache, oracle_decode, oracle_mha_decode
+from oracle import dequantize_cache, dequantize_heads, oracle_decode, oracle_mha_decode
 from mla_decode_attention_02_amd import api
 from mla_decode_attention_02_amd.workloads import make_inputs, make_mha_inputs
 
@@ -104,4 +104,29 @@ def test_mha_random(seed):
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, x.softmax_scale,
                                      causal)
+    _compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mha_fp8_random(seed):
+    """fp8 K/V caches over random shapes: groups 1-16 go to the key-split
+    kernel, larger row blocks to the column-split one."""
+    rng = np.random.default_rng(4000 + seed)
+    B, s_q, _, seqlens, causal, parts = _case(rng, 8)
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    d = int(rng.choice([64, 128, 256]))
+    mode = str(rng.choice(["amax", "pow2", "none"]))
+    h_q = h_kv * group
+    tag = f"mha fp8 seed={seed} B={B} s_q={s_q} h_q={h_q} h_kv={h_kv} d={d} seqlens={seqlens} causal={causal} {mode} parts={parts}"
+    _say(tag)
+    x = make_mha_inputs(B, s_q, h_q, h_kv, d, "bf16", seqlens=seqlens, causal=causal, seed=seed, poison=True,
+                        extra_pages=1, kv_dtype="fp8", scale_mode=mode)
+    g = x.to(torch.device("cuda:0"))
+    meta = api.mha_get_metadata(g.cache_seqlens, s_q, h_q, h_kv, num_parts=parts)
+    out, lse = api.mha_decode(g.q, g.k_cache, g.v_cache, g.block_table, g.cache_seqlens, g.softmax_scale, causal,
+                              metadata=meta, k_scale=g.k_scale, v_scale=g.v_scale)
+    torch.cuda.synchronize()
+    kf, vf = dequantize_heads(x.k_cache, x.k_scale), dequantize_heads(x.v_cache, x.v_scale)
+    ref_o, ref_l = oracle_mha_decode(x.q, kf, vf, x.block_table, x.cache_seqlens, x.softmax_scale, causal)
     _compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag)
