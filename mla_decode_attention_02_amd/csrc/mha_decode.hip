@@ -193,8 +193,8 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       const int valid = real ? min(kPage, n - page * kPage) : 0;
       const BufRsrc kr = mha_rows_rsrc<ESZ>(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
       const BufRsrc vr = mha_rows_rsrc<ESZ>(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, DV, valid);
-      int ln = lane;                             // opaque: offsets are rebuilt per step
-      asm volatile("" : "+v"(ln));
+      int ln = lane;                             // opaque: offsets are rebuilt per step (keeping
+      asm volatile("" : "+v"(ln));               // them in registers measured 4 % slower here)
 #pragma unroll
       for (int i = 0; i < NDMA; ++i) {
         const int j = wave * NDMA + i;           // instruction of this step, 0 .. 2*KBYTES/1024
@@ -460,6 +460,23 @@ __global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
   const int krow = 16 * wave + li;           // K row of the step this lane feeds to the score MFMAs
   const int ksw = mha_swz<CPR>(krow);
 
+  // this lane's source offset (within the step's first page row) for each of
+  // the wave's DMA instructions: instruction j moves 1 KiB, K rows then V
+  // rows, lane l filling slot l, i.e. row j*RPI + l / CPR, chunk
+  // (l % CPR) ^ swizzle(row).  Computed once: rebuilt per step, the 64-bit
+  // stride products cost more than the loads' issue.
+  int doff[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int j = wave * NDMA + i;
+    const bool isv = j >= KBYTES / 1024;
+    const int jj = isv ? j - KBYTES / 1024 : j;
+    const int r = jj * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ mha_swz<CPR>(r);
+    const int64_t rs = isv ? p.v_s1 : p.k_s1;
+    doff[i] = (int)(r * rs * ESZ) + c * 16;
+  }
+
   const int32_t* sc = p.sched + blockIdx.x * 8;
   const int begin_u = ldu(sc + 0), begin_page = ldu(sc + 1);
   const int end_u = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
@@ -503,9 +520,8 @@ __global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
     }
 
     // LDS-DMA loads of page lo + s into buffer ic (every wave moves NDMA KiB
-    // of the K then V rows; lane l fills slot l of its KiB, i.e. row
-    // j*RPI + l / CPR, chunk (l % CPR) ^ swizzle(row)); steps past the chunk
-    // use empty descriptors, so every step issues the same loads.
+    // of the K then V rows, at the offsets doff); steps past the chunk use
+    // empty descriptors, so every step issues the same loads.
     auto issue = [&](auto ic, int s) {
       MLA_LDS char* bp = buf(ic);
       const bool real = s < nsteps;
@@ -514,18 +530,12 @@ __global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
       const int valid = real ? min(kPage, n - page * kPage) : 0;
       const BufRsrc kr = mha_rows_rsrc<ESZ>(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
       const BufRsrc vr = mha_rows_rsrc<ESZ>(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, D, valid);
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < NDMA; ++i) {
         const int j = wave * NDMA + i;
         const bool isv = j >= KBYTES / 1024;
         const int jj = isv ? j - KBYTES / 1024 : j;
-        const int r = jj * RPI + ln / CPR;
-        const int c = (ln % CPR) ^ mha_swz<CPR>(r);
-        const int64_t rs = isv ? p.v_s1 : p.k_s1;
-        const int voff = (int)(r * rs * ESZ) + c * 16;
-        dma16<kAux>(isv ? vr : kr, bp + (isv ? KBYTES : 0) + jj * 1024, voff, 0);
+        dma16<kAux>(isv ? vr : kr, bp + (isv ? KBYTES : 0) + jj * 1024, doff[i], 0);
       }
       if constexpr (KV8) {
         MLA_LDS float* sp = sbuf(ic) + wave * 64;

@@ -110,6 +110,19 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
   const int vs = li >> 1, vh = li & 1;        // transposed reads: key slot row vs, column half vh
   const int vrow = 32 * kh + (vs < 4 ? 4 * g + vs : 12 + 4 * g + vs);
   const int vrot = rot8(vrow);
+  // this lane's source offset within a page for each of the wave's DMA
+  // instructions (instruction j = 9 w + i covers slots 64 j .. 64 j + 63 of
+  // the image, lane l slot 64 j + l, i.e. row q / 36, slot q % 36, holding
+  // source chunk slot ^ rot(row)): computed once, since the division by 36
+  // and the 32-bit products cost ~100 cycles per instruction if rebuilt for
+  // every page
+  int doff[kDma8];
+#pragma unroll
+  for (int i = 0; i < kDma8; ++i) {
+    const int q = (wave * kDma8 + i) * 64 + lane;
+    const int r = q / 36;
+    doff[i] = r * row_bytes + (((q - r * 36) ^ rot8(r)) << 4);
+  }
 
   for_each_chunk(p, [&](const Chunk& c) {
     BlockWindow bw;
@@ -119,9 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
     const int cnt = li < p.rows ? visible_count(c.n, p.s_q, li / p.h_q, p.causal) : 0;
     const int npg = c.hi - c.lo;
 
-    // LDS-DMA of page s of the chunk into buffer ic: instruction j = 9 w + i
-    // covers slots 64 j .. 64 j + 63 of the image, lane l slot 64 j + l, i.e.
-    // row q / 36, slot q % 36, holding source chunk slot ^ rot(row).
+    // LDS-DMA of page s of the chunk into buffer ic (offsets doff above).
     // Rows past the request's length are out of the descriptor's range and
     // land as zeros.  Every wave also lands the page's scale in its own slot.
     // Past the chunk the descriptors are empty, so every step issues the same
@@ -134,16 +145,8 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
       const int valid = real ? min(kPage, c.n - pg * kPage) : 0;
       const BufRsrc pr = page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0,
                                    valid > 0 ? (valid - 1) * row_bytes + kRow8 : 0);
-      int ln = lane;                               // opaque: offsets are rebuilt per step
-      asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int i = 0; i < kDma8; ++i) {
-        const int j = wave * kDma8 + i;
-        const int q = j * 64 + ln;
-        const int r = q / 36;
-        const int cs = (q - r * 36) ^ rot8(r);
-        dma16<kNarrowAux>(pr, bp + j * 1024, r * row_bytes + cs * 16, 0);
-      }
+      for (int i = 0; i < kDma8; ++i) dma16<kNarrowAux>(pr, bp + (wave * kDma8 + i) * 1024, doff[i], 0);
       const BufRsrc sr = page_rsrc((const char*)p.k_scale, scaled && real ? 0x7FFFFFFF : 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (MLA_LDS void*)(sbuf(ic) + wave * 64), 4, 0, phys * 4, 0, 0);
     };
