@@ -73,7 +73,7 @@ __device__ __forceinline__ BufRsrc mha_rows_rsrc(const void* base, int64_t elem_
   return page_rsrc((const char*)base + elem_off * ESZ, bytes);
 }
 
-template <typename T, int D, int RT, bool KV8>
+template <typename T, int D, int RT, bool KV8, bool RS>
 __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   constexpr int DV = D;
   constexpr int KS = D <= 128 ? 64 : 32;     // keys per step
@@ -86,7 +86,12 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   constexpr int KBYTES = KS * ROWB;
   constexpr int BUF = 2 * KBYTES;            // K rows, then V rows
   constexpr int DC = D / 32;                 // 32-deep contraction steps of Q.K
-  constexpr int CW = DV / 4;                 // output columns per wave
+  // RS (row split, for blocks of more than 16 rows): wave w owns rows
+  // 16w .. 16w+15 of the block and all output columns, so no wave repeats
+  // another's scores; else every wave takes all RT row tiles and a quarter
+  // of the columns
+  constexpr int RTW = RS ? 1 : RT;           // row tiles per wave
+  constexpr int CW = RS ? DV : DV / 4;       // output columns per wave
   constexpr int CT = CW / 16;                // 16-column output tiles per wave
   constexpr int NDMA = 2 * KBYTES / 1024 / 4;  // LDS-DMA instructions per wave and step
   constexpr int NLD = NDMA + (KV8 ? 2 : 0);  // and with the two scale loads
@@ -128,7 +133,8 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int mrow0 = blockIdx.y * 64;
+  const int mrow0 = blockIdx.y * 64 + (RS ? 16 * wave : 0);
+  const int cb = RS ? 0 : wave * CW;         // first output column of this wave
   const int ksw = mha_swz<CPR>(li);          // swizzle of K rows kt*16 + li
 
   const int32_t* sc = p.sched + blockIdx.x * 8;
@@ -156,10 +162,10 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
     // ks*32 + 8g .. +8 (fp8: fragment 2m columns 64m + 16g .. +8 and 2m + 1
     // the next 8, the order of the 16 codes one K read brings); rows past the
     // unit's rows are zero
-    u32x4 qf[RT][DC];
-    int cnt[RT];
+    u32x4 qf[RTW][DC];
+    int cnt[RTW];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
       const int row = mrow0 + rt * 16 + li;
       if (row < p.rows) {
         const int tok = row / p.group;
@@ -217,10 +223,10 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       }
     };
 
-    float m_run[RT], l_part[RT];
-    f32x4 o[RT][CT];
+    float m_run[RTW], l_part[RTW];
+    f32x4 o[RTW][CT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
       m_run[rt] = -INFINITY;
       l_part[rt] = 0.f;
 #pragma unroll
@@ -241,11 +247,11 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         if (p.v_scale) vscl = sbuf(Hc)[4 * 64];
       }
       // S^T tiles: keys kt*16 + 4g .. +4 of row li of tile rt
-      f32x4 sc4[KT][RT];
+      f32x4 sc4[KT][RTW];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RTW; ++rt) sc4[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const MLA_LDS char* krow = kb + (kt * 16 + li) * ROWB;
         if constexpr (KV8) {
 #pragma unroll
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
             const u32x4 ka = e4m3x8_to_bf16(kw[0], kw[1]);
             const u32x4 kc = e4m3x8_to_bf16(kw[2], kw[3]);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
+            for (int rt = 0; rt < RTW; ++rt) {
               sc4[kt][rt] = Dt<T>::mfma32(ka, qf[rt][2 * m], sc4[kt][rt]);
               sc4[kt][rt] = Dt<T>::mfma32(kc, qf[rt][2 * m + 1], sc4[kt][rt]);
             }
@@ -264,17 +270,17 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
           for (int ks = 0; ks < DC; ++ks) {
             const u32x4 kf = ld_lds16(krow + (((ks * 4 + g) ^ ksw) << 4));
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) sc4[kt][rt] = Dt<T>::mfma32(kf, qf[rt][ks], sc4[kt][rt]);
+            for (int rt = 0; rt < RTW; ++rt) sc4[kt][rt] = Dt<T>::mfma32(kf, qf[rt][ks], sc4[kt][rt]);
           }
         }
       }
       // online softmax per row tile; probabilities packed as the B operand of
       // the P.V MFMA: k-slots 8g .. 8g+7 = keys 4g..4g+3 of tiles 2kp, 2kp+1
-      u32x4 pf[RT][KT / 2];
-      float alpha[RT];
+      u32x4 pf[RTW][KT / 2];
+      float alpha[RTW];
       const int key0 = (ks0 + s) * KS + 4 * g;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+      for (int rt = 0; rt < RTW; ++rt) {
         float x[KT][4];
         float mx = -INFINITY;
 #pragma unroll
@@ -314,10 +320,10 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       }
       bool resc = false;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) resc |= alpha[rt] != 1.f;
+      for (int rt = 0; rt < RTW; ++rt) resc |= alpha[rt] != 1.f;
       if (__any(resc)) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) o[rt][ct] *= alpha[rt];
       }
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         const int vkey = vs < 4 ? 4 * g + vs : 12 + 4 * g + vs;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const int chunk = (wave * CW + ct * 16) / 16;
+          const int chunk = (cb + ct * 16) / 16;
 #pragma unroll
           for (int kp = 0; kp < KT / 2; ++kp) {
             const int r = 32 * kp + vkey;
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
             const u32x2 w = mha_ld_tr8(vb + off);
             const u32x4 vf = e4m3x8_to_bf16(w[0], w[1]);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
+            for (int rt = 0; rt < RTW; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
           }
         }
       } else {
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
         const int vsw = mha_swz<CPR>(vr);          // the same for vr + 16, vr + 32
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const int chunk = (wave * CW + ct * 16) / 8 + ((li >> 1) & 1);
+          const int chunk = (cb + ct * 16) / 8 + ((li >> 1) & 1);
           const int coff = ((chunk ^ vsw) << 4) + (li & 1) * 8;
 #pragma unroll
           for (int kp = 0; kp < KT / 2; ++kp) {
@@ -357,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
             const u32x2 hi4 = ld_lds_tr(vb + (32 * kp + 16 + vr) * ROWB + coff);
             const u32x4 vf = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
+            for (int rt = 0; rt < RTW; ++rt) o[rt][ct] = Dt<T>::mfma32(vf, pf[rt][kp], o[rt][ct]);
           }
         }
       }
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
 
     // epilogue: O / l, LSE; wave w writes its columns, wave 0 the LSEs
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
       const float l = sum_across_groups(l_part[rt]);
       const int row = mrow0 + rt * 16 + li;
       if (row >= p.rows) continue;
@@ -384,19 +390,19 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       const int tok = row / p.group;
       const int head = hk * p.group + (row - tok * p.group);
       if (nsplit == 1) {
-        T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + wave * CW + 4 * g;
+        T* dst = (T*)p.out + b * p.o_s0 + tok * p.o_s1 + head * p.o_s2 + cb + 4 * g;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const f32x4 v = o[rt][ct] * inv;
           *(u32x2*)(dst + ct * 16) = u32x2{Dt<T>::pack2(v[0], v[1]), Dt<T>::pack2(v[2], v[3])};
         }
-        if (wave == 0 && g == 0) p.lse[((int64_t)b * p.s_q + tok) * p.h_q + head] = lse;
+        if ((RS || wave == 0) && g == 0) p.lse[((int64_t)b * p.s_q + tok) * p.h_q + head] = lse;
       } else {
         const int64_t slot = slot0 + split;
-        float* dst = p.part_o + (slot * p.rows + row) * DV + wave * CW + 4 * g;
+        float* dst = p.part_o + (slot * p.rows + row) * DV + cb + 4 * g;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) *(f32x4*)(dst + ct * 16) = o[rt][ct] * inv;
-        if (wave == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+        if ((RS || wave == 0) && g == 0) p.part_lse[slot * p.rows + row] = lse;
       }
     }
   }
@@ -866,11 +872,13 @@ hipError_t launch_mha_d(const MhaParams& p, hipStream_t st) {
   if (launch_keysplit<T, D, KV8, 1>(rt, grid, p, st) || launch_keysplit<T, D, KV8, 2>(rt, grid, p, st) ||
       launch_keysplit<T, D, KV8, 3>(rt, grid, p, st) || launch_keysplit<T, D, KV8, 4>(rt, grid, p, st))
     return hipGetLastError();
+  // one row tile: the column split; more: the row split (no wave repeats
+  // another's scores)
   switch (rt) {
-    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1, KV8>), grid, dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2, KV8>), grid, dim3(256), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3, KV8>), grid, dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4, KV8>), grid, dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1, KV8, false>), grid, dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2, KV8, true>), grid, dim3(256), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3, KV8, true>), grid, dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4, KV8, true>), grid, dim3(256), 0, st, p); break;
   }
   return hipGetLastError();
 }
