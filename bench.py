@@ -368,7 +368,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, help="1..9; 2 is the headline workload, 6 is 3 with an fp8 cache, 7-9 are GQA (MHA path; 9 with fp8 K/V)")
+    ap.add_argument("--workload", type=int, default=2, help="1..10; 2 is the headline workload, 6 is 3 with an fp8 cache, 7-10 use the MHA path (7-9 GQA, 9 with fp8 K/V; 10 multi-query)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

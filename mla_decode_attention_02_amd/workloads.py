@@ -260,6 +260,8 @@ MHA_WORKLOADS = {
     9: MhaWorkload("gqa_bs64_hq64_hkv8_d128_fp8kv", 64, 1, 64, 8, 128, "bf16", False, seqlen_range=(1, 8192),
                    seed=7, kv="fp8",
                    description="workload 7 with fp8 e4m3 K/V caches, one scale per page and KV head"),
+    10: MhaWorkload("mqa_bs128_hq64_hkv1_d128", 128, 1, 64, 1, 128, "bf16", False, seqlen_range=(1, 8192),
+                    seed=10, description="B128 s_q1 h_q64 h_kv1 d128 bf16 (multi-query), s_k ~ U[1,8192]"),
 }
 
 
