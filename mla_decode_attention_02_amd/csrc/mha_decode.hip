@@ -137,6 +137,22 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   const int cb = RS ? 0 : wave * CW;         // first output column of this wave
   const int ksw = mha_swz<CPR>(li);          // swizzle of K rows kt*16 + li
 
+  // row split: this lane's source offsets (within the step's first row) for
+  // its DMA instructions, computed once
+  int doff[RS ? NDMA : 1];
+  if constexpr (RS) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int j = wave * NDMA + i;
+      const bool isv = j >= KBYTES / 1024;
+      const int jj = isv ? j - KBYTES / 1024 : j;
+      const int r = jj * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ mha_swz<CPR>(r);
+      const int64_t rs = isv ? p.v_s1 : p.k_s1;
+      doff[i] = (int)(r * rs * ESZ) + c * 16;
+    }
+  }
+
   const int32_t* sc = p.sched + blockIdx.x * 8;
   const int begin_u = ldu(sc + 0), begin_page = ldu(sc + 1);
   const int end_u = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
@@ -200,17 +216,22 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
       const BufRsrc kr = mha_rows_rsrc<ESZ>(p.k, (int64_t)phys * p.k_s0 + hk * p.k_s2, p.k_s1, D, valid);
       const BufRsrc vr = mha_rows_rsrc<ESZ>(p.v, (int64_t)phys * p.v_s0 + hk * p.v_s2, p.v_s1, DV, valid);
       int ln = lane;                             // opaque: offsets are rebuilt per step (keeping
-      asm volatile("" : "+v"(ln));               // them in registers measured 4 % slower here)
-#pragma unroll
+      asm volatile("" : "+v"(ln));               // them in registers measured 4 % slower with the
+#pragma unroll                                   // column split; the row split keeps them)
       for (int i = 0; i < NDMA; ++i) {
         const int j = wave * NDMA + i;           // instruction of this step, 0 .. 2*KBYTES/1024
         const bool isv = j >= KBYTES / 1024;
         const int jj = isv ? j - KBYTES / 1024 : j;
-        const int r = jj * RPI + ln / CPR;       // row of the step
-        const int c = (ln % CPR) ^ mha_swz<CPR>(r);
-        const int key = sub * KS + r;            // slot within the page
         const int64_t rs = isv ? p.v_s1 : p.k_s1;
-        const int voff = (int)(key * rs * ESZ) + c * 16;
+        int voff;
+        if constexpr (RS) {
+          voff = doff[i] + (int)(sub * KS * rs * ESZ);
+        } else {
+          const int r = jj * RPI + ln / CPR;     // row of the step
+          const int c = (ln % CPR) ^ mha_swz<CPR>(r);
+          const int key = sub * KS + r;          // slot within the page
+          voff = (int)(key * rs * ESZ) + c * 16;
+        }
         dma16<kAux>(isv ? vr : kr, bp + (isv ? KBYTES : 0) + jj * 1024, voff, 0);
       }
       if constexpr (KV8) {
