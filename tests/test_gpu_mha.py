@@ -93,6 +93,8 @@ EDGE = [
     (3, 32, 1, 64, (129, 700), True, "bf16", 3),           # 96 rows: two row blocks
     (2, 40, 2, 128, (2, 129, 300), True, "bf16", 3),       # 40 rows: three row tiles
     (1, 12, 4, 128, (5000,), False, "bf16", 17),           # one long request cut into many pieces
+    (1, 32, 1, 128, (70, 300), False, "fp16", 4),          # 32 rows: row split, two idle waves
+    (2, 64, 2, 256, (40, 129), True, "fp16", 3),           # 64 rows, d = 256: row split, fp16
 ]
 
 
