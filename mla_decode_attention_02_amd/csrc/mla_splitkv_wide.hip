@@ -256,10 +256,17 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         const int t = t0 + decltype(Hc)::value;
         if (t <= nh) stepx(Hc, t);
       });
-      // epilogue: normalise, write the final output or an fp32 partial
+      // epilogue: normalise, write the final output or an fp32 partial.  The
+      // lane's row and column come from an opaque copy of the lane index, so
+      // that their address arithmetic is done here: hoisted to the kernel
+      // start, the per-row-tile addresses were spilled to scratch, and each
+      // reload waited for every store issued before it.
+      int eln = lane;
+      asm volatile("" : "+v"(eln));
+      const int eli = eln & 15, eg = eln >> 4;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int rl = rt * 16 + li;
+        const int rl = rt * 16 + eli;
         const int row = mrow0 + rl;
         if (row >= p.rows) continue;
         const float l = l_s[rl];
@@ -268,14 +275,14 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         if (c.nsplit == 1) {
 #pragma unroll
           for (int ct = 0; ct < 8; ++ct)
-            store_out4<T>(p, c.b, row, cw * 128 + ct * 16 + 4 * g, o[ct][rt] * inv);
-          if (cw == 0 && g == 0) p.lse[(int64_t)c.b * p.rows + row] = lse;
+            store_out4<T>(p, c.b, row, cw * 128 + ct * 16 + 4 * eg, o[ct][rt] * inv);
+          if (cw == 0 && eg == 0) p.lse[(int64_t)c.b * p.rows + row] = lse;
         } else {
           const int64_t slot = c.slot0 + c.split;
-          float* dst = p.part_o + (slot * p.rows + row) * kDV + cw * 128 + 4 * g;
+          float* dst = p.part_o + (slot * p.rows + row) * kDV + cw * 128 + 4 * eg;
 #pragma unroll
           for (int ct = 0; ct < 8; ++ct) *(f32x4*)(dst + ct * 16) = o[ct][rt] * inv;
-          if (cw == 0 && g == 0) p.part_lse[slot * p.rows + row] = lse;
+          if (cw == 0 && eg == 0) p.part_lse[slot * p.rows + row] = lse;
         }
       }
       if (c.nsplit > 1 && c.nsplit <= p.fuse_max) fused_merge<T, 64, 512>(p, c, mrow0, merge_s);
