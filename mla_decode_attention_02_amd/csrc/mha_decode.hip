@@ -73,7 +73,7 @@ __device__ __forceinline__ BufRsrc mha_rows_rsrc(const void* base, int64_t elem_
   return page_rsrc((const char*)base + elem_off * ESZ, bytes);
 }
 
-template <typename T, int D, int RT, bool KV8, bool RS>
+template <typename T, int D, int RT, bool KV8, bool RS, bool NT>
 __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   constexpr int DV = D;
   constexpr int KS = D <= 128 ? 64 : 32;     // keys per step
@@ -98,9 +98,9 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
   constexpr int RPI = 1024 / ROWB;           // rows per DMA instruction
   static_assert(KT % 2 == 0 && CT >= 1 && NDMA >= 1 && 2 * KBYTES % 4096 == 0, "tile shape");
   static_assert((NB - 1) * NLD <= 63, "loads in flight fit the wait counter");
-  // K/V bytes are read once when the unit's rows fit one row block:
-  // non-temporal; row blocks of one unit may meet in L2 otherwise
-  constexpr int kAux = RT < 4 ? 2 : 0;
+  // NT: the unit's rows fit one row block, so its K/V bytes are read once
+  // (non-temporal loads); otherwise the row blocks of one unit may meet in L2
+  constexpr int kAux = NT ? 2 : 0;
   // one array per buffer, so that the compiler can tell the reads of one from
   // the loads in flight into another (it tells apart at most eight LDS-DMA
   // targets, so the fp8 scales live at the end of their buffer's array)
@@ -896,10 +896,13 @@ hipError_t launch_mha_d(const MhaParams& p, hipStream_t st) {
   // one row tile: the column split; more: the row split (no wave repeats
   // another's scores)
   switch (rt) {
-    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1, KV8, false>), grid, dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2, KV8, true>), grid, dim3(256), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3, KV8, true>), grid, dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4, KV8, true>), grid, dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 1, KV8, false, true>), grid, dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 2, KV8, true, true>), grid, dim3(256), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 3, KV8, true, true>), grid, dim3(256), 0, st, p); break;
+    default:
+      if (m_blocks == 1) hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4, KV8, true, true>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((mha_splitkv_kernel<T, D, 4, KV8, true, false>), grid, dim3(256), 0, st, p);
+      break;
   }
   return hipGetLastError();
 }
