@@ -41,3 +41,20 @@ def test_metadata_needs_device_lengths():
         api.get_metadata(torch.tensor([3, 4], dtype=torch.int32), 1, 16)
     with pytest.raises(ValueError):
         api.mha_get_metadata(torch.tensor([3, 4], dtype=torch.int32), 1, 8, 2)
+
+
+def test_mha_fp8_rejects_mismatches():
+    x = make_mha_inputs(2, 1, 8, 2, 64, "bf16", seqlens=(64, 3), seed=1, kv_dtype="fp8")
+    n, h = x.k_cache.shape[0], x.k_cache.shape[2]
+    with pytest.raises(ValueError):                    # fp8 K with a bf16 V
+        api._validate_mha(x.q, x.k_cache, x.v_cache.to(torch.bfloat16), x.block_table, x.cache_seqlens)
+    with pytest.raises(ValueError):                    # fp8 caches need a bf16 q
+        api._validate_mha(x.q.half(), x.k_cache, x.v_cache, x.block_table, x.cache_seqlens)
+    with pytest.raises(ValueError):                    # one scale per page and KV head
+        api._validate_mha(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, k_scale=torch.ones(n))
+    with pytest.raises(ValueError):
+        api._validate_mha(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens,
+                          v_scale=torch.ones(n, h, dtype=torch.float64))
+    y = make_mha_inputs(2, 1, 8, 2, 64, "bf16", seqlens=(64, 3), seed=1)
+    with pytest.raises(ValueError):                    # scales apply to fp8 caches only
+        api._validate_mha(y.q, y.k_cache, y.v_cache, y.block_table, y.cache_seqlens, k_scale=torch.ones(n, h))
