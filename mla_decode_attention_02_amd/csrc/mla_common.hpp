@@ -245,19 +245,21 @@ __device__ __forceinline__ u32x4 buf_load16(BufRsrc r, int voff, int soff) {
 // Issue the loads of one 64x576 page (HBM -> registers).  Wave w fetches value
 // rows 16w..16w+15 (one 1 KiB row per instruction, fully coalesced) and rope
 // rows 16w..16w+15 (8 rows per instruction).  Lane l fetches the source chunk
-// that belongs in LDS slot l of its row, i.e. chunk l ^ swizzle(row).
+// that belongs in LDS slot l of its row, i.e. chunk l ^ swizzle(row).  The row
+// offset is part of the per-lane offset, which is what the descriptor's range
+// check sees: rows past the descriptor's end read as zeros.
 template <int kAux>
 __device__ __forceinline__ void stage_load(PageStage& st, BufRsrc page, int row_bytes, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int key = (j & 7) << 1;                          // == swz_v(16 * wave + j)
-    st.v[j] = buf_load16<kAux>(page, (lane ^ key) << 4, (wave * 16 + j) * row_bytes);
+    st.v[j] = buf_load16<kAux>(page, ((lane ^ key) << 4) + (wave * 16 + j) * row_bytes, 0);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = (wave * 2 + i) * 8 + (lane >> 3);
-    const int voff = (lane >> 3) * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
-    st.v[16 + i] = buf_load16<kAux>(page, voff, (wave * 2 + i) * 8 * row_bytes);
+    const int voff = r * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
+    st.v[16 + i] = buf_load16<kAux>(page, voff, 0);
   }
 }
 
@@ -322,28 +324,15 @@ __device__ __forceinline__ void dma16(BufRsrc page, MLA_LDS char* dst, int voff,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(page, (MLA_LDS void*)dst, 16, voff, soff, 0, kAux);
 }
 
-// Value rows r0 .. r0+3 of half page `half` (0/1) of a page into half buffer
-// `hb`: one 1 KiB row per instruction, lane l fetching the chunk that belongs
-// in slot l of its row, i.e. chunk l ^ swz_v(row).
-template <int kAux>
-__device__ __forceinline__ void dma_value_rows4(BufRsrc page, MLA_LDS char* hb, int half, int r0, int row_bytes,
-                                                int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = r0 + j;
-    const int key = (r & 7) << 1;                      // == swz_v(r), uniform
-    dma16<kAux>(page, hb + r * 1024, (lane ^ key) << 4, (half * kHalfRows + r) * row_bytes);
-  }
-}
-
 // Rope rows 8i .. 8i+7 of half page `half` (one instruction; lane l takes row
-// 8i + l/8, slot l%8).
+// 8i + l/8, slot l%8).  The row offset is in the per-lane offset, so the
+// descriptor's range check covers it.
 template <int kAux>
 __device__ __forceinline__ void dma_rope_rows8(BufRsrc page, MLA_LDS char* hb, int half, int i, int row_bytes,
                                                int lane) {
   const int r = i * 8 + (lane >> 3);
-  const int voff = (lane >> 3) * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
-  dma16<kAux>(page, hb + kHalfRopeOff + i * 1024, voff, (half * kHalfRows + i * 8) * row_bytes);
+  const int voff = (half * kHalfRows + r) * row_bytes + 1024 + (((lane & 7) ^ swz_r(r)) << 4);
+  dma16<kAux>(page, hb + kHalfRopeOff + i * 1024, voff, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding

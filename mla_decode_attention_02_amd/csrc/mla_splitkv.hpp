@@ -81,10 +81,17 @@ __device__ __forceinline__ void for_each_chunk(const DecodeParams& p, F&& f) {
   }
 }
 
-// Descriptor of physical page `phys` of the cache.
-__device__ __forceinline__ BufRsrc page_of(const DecodeParams& p, int phys, int page_bytes) {
-  return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0 * 2, page_bytes);
+// Descriptor of physical page `phys` of the cache covering its first `valid`
+// rows (none when valid <= 0).  Loads address rows through the per-lane
+// offset, which the range check covers, so slots past a request's length are
+// never read: they arrive as zeros (0 * NaN can then never reach P.V).
+__device__ __forceinline__ BufRsrc page_of(const DecodeParams& p, int phys, int valid) {
+  const int row_bytes = (int)(p.k_s1 * 2);
+  return page_rsrc((const char*)p.k + (int64_t)phys * p.k_s0 * 2, valid > 0 ? (valid - 1) * row_bytes + kDK * 2 : 0);
 }
+
+// Rows of page `pg` of a request with n cached tokens that hold tokens.
+__device__ __forceinline__ int page_valid_rows(int n, int pg) { return min(kPage, n - pg * kPage); }
 
 // --------------------------------------------------------- fused merge --
 // The combine folded into the split-KV kernel (the MI355X answer to launching

@@ -21,7 +21,6 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63, g = lane >> 4, li = lane & 15;
   const int row_bytes = (int)(p.k_s1 * 2);
-  const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
 
   for_each_chunk(p, [&](const Chunk& c) {
     BlockWindow bw;
@@ -42,13 +41,13 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_narrow_kernel(DecodeParam
 
     // two pages in flight in registers while a third is read from LDS
     PageStage st[2];
-    stage_load<kNarrowAux>(st[0], page_of(p, bw.phys(c.lo), page_bytes), row_bytes, wave, lane);
-    if (c.lo + 1 < c.hi) stage_load<kNarrowAux>(st[1], page_of(p, bw.phys(c.lo + 1), page_bytes), row_bytes, wave, lane);
+    stage_load<kNarrowAux>(st[0], page_of(p, bw.phys(c.lo), page_valid_rows(c.n, c.lo)), row_bytes, wave, lane);
+    if (c.lo + 1 < c.hi) stage_load<kNarrowAux>(st[1], page_of(p, bw.phys(c.lo + 1), page_valid_rows(c.n, c.lo + 1)), row_bytes, wave, lane);
     stage_store(st[0], kbuf0, wave, lane);
     lds_barrier();
     page_loop(c.lo, c.hi, kbuf0, kbuf1, [&](auto par, MLA_LDS char* cur, MLA_LDS char* nxt, int pg) {
       constexpr int P = decltype(par)::value;   // st[P] held page pg, st[P ^ 1] holds pg + 1
-      if (pg + 2 < c.hi) stage_load<kNarrowAux>(st[P], page_of(p, bw.phys(pg + 2), page_bytes), row_bytes, wave, lane);
+      if (pg + 2 < c.hi) stage_load<kNarrowAux>(st[P], page_of(p, bw.phys(pg + 2), page_valid_rows(c.n, pg + 2)), row_bytes, wave, lane);
 
       // S^T for keys wave*16 .. +16 of the page, all 16 rows; operand reads
       // run two steps ahead of the MFMAs

@@ -58,7 +58,6 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   const int g = lane >> 4, li = lane & 15;
   const int mrow0 = blockIdx.y * 64;
   const int row_bytes = (int)(p.k_s1 * 2);
-  const int page_bytes = (kPage - 1) * row_bytes + kDK * 2;
 
   // Half pages of a chunk: its pages, less a last half that lies wholly past
   // the end of the request.
@@ -89,7 +88,8 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
       // (every lane out of range, no memory access).
       auto page_desc = [&](int hh) {
         const bool real = hh < nh;
-        return page_of(p, real ? bw.phys(c.lo + (hh >> 1)) : 0, real ? page_bytes : 0);
+        const int pg = c.lo + (hh >> 1);
+        return page_of(p, real ? bw.phys(pg) : 0, real ? page_valid_rows(c.n, pg) : 0);
       };
       auto piece = [&](auto ic, int hh, BufRsrc pg, int i) {
         MLA_LDS char* hb = hbuf(ic);
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
         asm volatile("" : "+v"(ln));
         if (i < 8) {
           const int r = 8 * wave + i;
-          dma16<kWideAux>(pg, hb + r * 1024, (ln ^ swz_v(r)) << 4, (half * kHalfRows + r) * row_bytes);
+          dma16<kWideAux>(pg, hb + r * 1024, ((ln ^ swz_v(r)) << 4) + (half * kHalfRows + r) * row_bytes, 0);
         } else {
           dma_rope_rows8<kWideAux>(pg, hb, half, wave, row_bytes, ln);
         }

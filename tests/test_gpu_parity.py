@@ -271,6 +271,33 @@ def test_unused_slots_are_never_read_bitwise():
     assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("s_q,h_q,dtype", [(1, 16, "bf16"), (1, 128, "bf16"), (2, 64, "fp16"), (3, 5, "fp16")])
+def test_nan_inf_in_unused_slots_never_reach_the_output(s_q, h_q, dtype, entry):
+    """Slots past a request's length in its last page hold NaN and +-Inf (as a
+    cache allocated with torch.empty may): the result must equal the one with
+    finite garbage there, bit for bit, and match the oracle.  A kernel that
+    loads those slots and multiplies them by P = 0 would turn the whole request
+    into NaN."""
+    seqlens = (70, 130, 3, 64, 200)
+    _say(f"NaN/Inf in unused slots {entry} s_q={s_q} h_q={h_q} {dtype}")
+    x = make_inputs(len(seqlens), s_q, h_q, dtype, seqlens=seqlens, seed=57 + h_q, poison=True,
+                    extra_pages=2, causal=s_q > 1)
+    ref_o, ref_l = oracle_decode(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, x.causal)
+    out1, lse1, _ = run(x, 3, entry)
+    for b, nlen in enumerate(seqlens):
+        if nlen % 64:
+            pg = int(x.block_table[b, (nlen + 63) // 64 - 1])
+            tail = x.k_cache[pg, nlen % 64:, 0, :]
+            tail[0::2] = float("nan")
+            tail[1::2] = float("inf")
+            tail[1::2, 1::2] = float("-inf")
+    out2, lse2, _ = run(x, 3, entry)
+    assert not np.isnan(out2).any() and not np.isnan(lse2).any()
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+    compare(out2, lse2, ref_o, ref_l, "nan tail")
+
+
 @pytest.mark.parametrize("h_q", [16, 128])
 def test_split_counts_agree(h_q):
     _say(f"one partition vs many partitions h_q={h_q}")
