@@ -240,6 +240,34 @@ def _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale=None):
             raise ValueError("all tensors must live on the same GPU")
     if q.stride(3) != 1 or k_cache.stride(3) != 1 or block_table.stride(1) != 1:
         raise ValueError("innermost dimensions must be contiguous")
+    _check_batch(q, block_table, cache_seqlens)
+
+
+def _check_batch(q, block_table, cache_seqlens):
+    # the schedule is built from cache_seqlens and the kernels index block_table
+    # rows by request: all three must describe the same requests
+    if not (block_table.shape[0] == cache_seqlens.numel() == q.shape[0]):
+        raise ValueError(f"batch mismatch: q has {q.shape[0]} requests, block_table {block_table.shape[0]}, "
+                         f"cache_seqlens {cache_seqlens.numel()}")
+
+
+def _check_outputs(q, out, lse, d_v):
+    B, s_q, h_q = q.shape[0], q.shape[1], q.shape[2]
+    if tuple(out.shape) != (B, s_q, h_q, d_v) or out.dtype != q.dtype or out.device != q.device \
+            or out.stride(3) != 1:
+        raise ValueError(f"out must be [{B}, {s_q}, {h_q}, {d_v}] in q's dtype on q's device, innermost contiguous")
+    if tuple(lse.shape) != (B, s_q, h_q) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous fp32 [{B}, {s_q}, {h_q}] tensor on q's device")
+
+
+def _check_metadata(sched, offs, units, device):
+    if sched.dtype != torch.int32 or offs.dtype != torch.int32 or sched.device != device or offs.device != device:
+        raise ValueError("metadata must be int32 tensors on q's device")
+    if sched.dim() != 2 or sched.shape[1] != SCHED_FIELDS or not sched.is_contiguous():
+        raise ValueError(f"sched must be a contiguous [num_parts, {SCHED_FIELDS}] tensor")
+    if offs.dim() != 1 or offs.numel() != units + 1 or not offs.is_contiguous():
+        raise ValueError(f"split_offsets must be a contiguous [{units + 1}] tensor")
 
 
 class DecodeBuffers:
@@ -261,8 +289,10 @@ def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal
     if metadata is None:
         metadata = get_metadata(cache_seqlens, q.shape[1], q.shape[2], k_cache.shape[2])
     sched, offs = metadata
+    _check_metadata(sched, offs, q.shape[0], q.device)
     if buffers is None:
         buffers = DecodeBuffers(q, sched.shape[0])
+    _check_outputs(q, buffers.out, buffers.lse, D_V)
     a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
                     buffers.workspace, buffers.out, buffers.lse, k_scale)
     _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
@@ -278,7 +308,8 @@ def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor
     lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result
     (computed here when omitted); `buffers` lets a caller reuse outputs.  An
     fp8 cache (torch.float8_e4m3fn, with a bf16 q and s_q*h_q <= 16) takes an
-    optional per-page power-of-two `k_scale` [num_pages] fp32."""
+    optional per-page fp32 scale `k_scale` [num_pages] (any finite value; the
+    cached row is code * scale)."""
     return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
                  k_scale)
 
@@ -419,6 +450,7 @@ def _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens, k_scale=None,
             raise ValueError("all tensors must live on the same GPU")
     if q.stride(3) != 1 or k_cache.stride(3) != 1 or v_cache.stride(3) != 1 or block_table.stride(1) != 1:
         raise ValueError("innermost dimensions must be contiguous")
+    _check_batch(q, block_table, cache_seqlens)
 
 
 def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
@@ -429,8 +461,10 @@ def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_
     if metadata is None:
         metadata = mha_get_metadata(cache_seqlens, s_q, h_q, h_kv)
     sched, offs = metadata
+    _check_metadata(sched, offs, B * h_kv, q.device)
     if buffers is None:
         buffers = MhaBuffers(q, h_kv, sched.shape[0])
+    _check_outputs(q, buffers.out, buffers.lse, d)
     a = MhaArgs()
     a.dtype = DTYPE_CODES[q.dtype]
     a.batch, a.s_q, a.h_q, a.h_kv = B, s_q, h_q, h_kv

@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
 // stream, not HBM, bounds the column-split kernel for small groups.
 // The staging of K and V (LDS-DMA, buffers named at compile time, steps in
 // flight, fp8 scales) is that of the kernel above.
-template <typename T, int D, int RT, bool KV8>
+template <typename T, int D, int RT, bool KV8, bool NT>
 __global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
   constexpr int KS = 64;                     // keys per step (one page), 16 per wave
   constexpr int ESZ = KV8 ? 1 : 2;
@@ -465,7 +465,9 @@ __global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
   static_assert(RT * D <= 256 && MCT >= 1 && NDMA >= 1 && 2 * KBYTES % 4096 == 0, "tile shape");
   static_assert((NB - 1) * NLD <= 63, "loads in flight fit the wait counter");
   static_assert(NB * BUFA <= 160 * 1024 - 2 * 4 * 64 * 4, "LDS");
-  constexpr int kAux = 2;                    // rows fit one row block: K/V read once, non-temporal
+  // non-temporal loads when a unit's rows fit one row block (its K/V rows are
+  // then read once); with several row blocks they share the pages in L2
+  constexpr int kAux = NT ? 2 : 0;
   __shared__ __attribute__((aligned(1024))) char b0_raw[BUFA];
   __shared__ __attribute__((aligned(1024))) char b1_raw[BUFA];
   __shared__ __attribute__((aligned(1024))) char b2_raw[BUFA];
@@ -878,7 +880,8 @@ template <typename T, int D, bool KV8, int RT>
 bool launch_keysplit(int rt, dim3 grid, const MhaParams& p, hipStream_t st) {
   if constexpr (kKeySplit<T, D, KV8, RT>) {
     if (rt == RT) {
-      hipLaunchKernelGGL((mha_keysplit_kernel<T, D, RT, KV8>), grid, dim3(256), 0, st, p);
+      if (grid.y == 1) hipLaunchKernelGGL((mha_keysplit_kernel<T, D, RT, KV8, true>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((mha_keysplit_kernel<T, D, RT, KV8, false>), grid, dim3(256), 0, st, p);
       return true;
     }
   }

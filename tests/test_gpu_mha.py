@@ -212,6 +212,13 @@ FP8_EDGE = [
     (1, 64, 1, 128, (200, 1000), False, "amax", 6),        # 64 rows: one full row block
     (2, 40, 2, 128, (2, 129, 300), True, "amax", 3),       # 40 rows: three row tiles
     (1, 12, 4, 128, (5000,), False, "amax", 17),           # one long request cut into many pieces
+    # key-split kernel with more than one row tile, and the fp8 row split at d = 256
+    (1, 32, 1, 128, (70, 640, 3), False, "amax", 3),       # d=128, 32 rows: key split, two row tiles
+    (1, 32, 1, 64, (65, 300), False, "pow2", None),        # d=64, 32 rows: key split, two row tiles
+    (1, 48, 1, 64, (129, 64, 1), False, "amax", 4),        # d=64, 48 rows: key split, three row tiles
+    (3, 32, 1, 64, (2, 129, 300), True, "amax", 3),        # d=64, 96 rows: key split, four tiles, two row blocks
+    (1, 32, 1, 256, (33, 200), False, "amax", 2),          # d=256, 32 rows: fp8 row split
+    (2, 16, 1, 256, (1, 65, 130), True, "none", 3),        # d=256, 32 rows, causal: fp8 row split
 ]
 
 
