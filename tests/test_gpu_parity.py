@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
 Tolerances (bf16/fp16 inputs, fp32 accumulation): max |dO| <= 1.5e-2 and
-max |dLSE| <= 1e-3 against the oracle on the same seeded inputs; the schedule
-is integer work and must be bit-exact.  Every case prints its name first so a
+max |dLSE| <= 1e-3 against the oracle on the same seeded inputs, and at full
+size an RMS-relative output error <= 1e-2 over the whole workload; the
+schedule is integer work and must be bit-exact.  Every case prints its name first so a
 failing run identifies itself.
 """
 
@@ -334,28 +335,48 @@ def test_fused_repeated_calls_reuse_counters(h_q):
         assert not bufs.workspace[:256].any(), "arrival counters were not reset"
 
 
-# ----------------------------------------------------- full-size samples --
+# ------------------------------------------------------------ full size --
+# RMS of the output error relative to the RMS of the output, over a whole
+# workload: an alarm beside the absolute bounds, which are loose where |O| is
+# small (two-token fp16 decode with sigma 0.5 has |O| of a few 1e-3).
+TOL_RMS_REL = 1e-2
+_FULL_REF = {}
+
+
+def _full_reference(idx, x):
+    """Oracle output of every request of a full-size workload (computed once
+    per module, shared by both entry points)."""
+    if idx not in _FULL_REF:
+        w = WORKLOADS[idx]
+        qf = x.q.double().numpy()
+        kf = kv64(x)
+        _FULL_REF[idx] = [oracle_decode_rows(qf, kf, x.block_table, x.cache_seqlens, x.softmax_scale, w.causal, b)
+                          for b in range(w.batch)]
+    return _FULL_REF[idx]
+
+
 @pytest.mark.parametrize("entry", ENTRIES)
 @pytest.mark.parametrize("idx", [2, 3, 4, 5, 6])
-def test_workload_full_size_sampled(idx, entry):
+def test_workload_full_size_every_request(idx, entry):
     """Full-size workload in the launch configuration the benchmark uses;
-    the oracle checks a sample of requests (first, last, and the longest)."""
+    every request is checked against the oracle (max |dO|, max |dLSE|), and
+    the RMS-relative output error over the whole workload is bounded."""
     w = WORKLOADS[idx]
     _say(f"workload {idx} {w.name} full size ({entry})")
     x = workload_inputs(idx)
     out, lse, meta = run(x, entry=entry)
-    seqlens = x.cache_seqlens.tolist()
-    offs = meta[1]
-    split = [b for b in range(w.batch) if offs[b + 1] - offs[b] > 1]
-    whole = [b for b in range(w.batch) if offs[b + 1] - offs[b] == 1]
-    picks = sorted(set([0, w.batch - 1, int(np.argmax(seqlens))] + split[:1] + whole[:1]))
-    qf = x.q.double().numpy()
-    kf = kv64(x)
-    for b in picks:
-        ref_o, ref_l = oracle_decode_rows(qf, kf, x.block_table, x.cache_seqlens, x.softmax_scale,
-                                          w.causal, b)
-        R = w.s_q * w.h_q
-        compare(out[b].reshape(R, 512), lse[b].reshape(R), ref_o, ref_l, f"workload {idx} request {b}")
+    ref = _full_reference(idx, x)
+    R = w.s_q * w.h_q
+    num = den = 0.0
+    for b in range(w.batch):
+        ref_o, ref_l = ref[b]
+        o = out[b].reshape(R, 512)
+        compare(o, lse[b].reshape(R), ref_o, ref_l, f"workload {idx} request {b}")
+        num += float(((o - ref_o) ** 2).sum())
+        den += float((ref_o ** 2).sum())
+    rms_rel = (num / den) ** 0.5
+    _say(f"workload {idx} rms_rel_dO = {rms_rel:.3e}")
+    assert rms_rel <= TOL_RMS_REL, f"workload {idx}: RMS-relative dO = {rms_rel}"
     assert np.isfinite(lse).all()
 
 
