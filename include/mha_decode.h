@@ -73,7 +73,7 @@ mla_status mha_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
  * requests.  Errors: INVALID_VALUE, HIP.
  */
 mla_status mha_get_metadata(const int32_t* cache_seqlens, int batch, int h_kv, int num_parts, int32_t* sched,
-                            int32_t* split_offsets, void* stream);
+                            int32_t* split_offsets, hipStream_t stream);
 
 /*
  * Bytes of device workspace mha_decode needs: fp32 partial outputs and LSEs
@@ -133,19 +133,19 @@ typedef struct {
  * alignment, non-finite or non-positive scale, h_q not a multiple of h_kv),
  * UNSUPPORTED (dtype, head_dim, page size), WORKSPACE_TOO_SMALL, HIP.
  */
-mla_status mha_decode(const mha_decode_args* args, void* stream);
+mla_status mha_decode(const mha_decode_args* args, hipStream_t stream);
 /* (also UNSUPPORTED: an fp8 cache with dtype other than bf16, or a kv_dtype
  * this library does not know; INVALID_VALUE: an fp8 cache stride not a
  * multiple of 16, a misaligned scale array) */
 
 /* First phase only: the split-KV kernel (whole units get their final out/lse,
  * pieces of split units go to the workspace).  Same arguments and errors. */
-mla_status mha_decode_splitkv(const mha_decode_args* args, void* stream);
+mla_status mha_decode_splitkv(const mha_decode_args* args, hipStream_t stream);
 
 /* Second phase only: merge of the split units' pieces by their LSE, and
  * O = 0 / LSE = -inf for requests with no cached token.  Must follow
  * mha_decode_splitkv with the same arguments on the same stream. */
-mla_status mha_decode_combine(const mha_decode_args* args, void* stream);
+mla_status mha_decode_combine(const mha_decode_args* args, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,10 @@
 extern "C" {
 #endif
 
+/* The HIP stream type, declared here as HIP's own headers declare it so that
+ * this header needs no HIP include (the same typedef repeated is allowed). */
+typedef struct ihipStream_t* hipStream_t;
+
 #define MLA_ABI_VERSION 4
 
 #define MLA_D_K 576             /* cached row width = query width           */
@@ -90,7 +94,10 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
 typedef enum { MLA_KV_SAME = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype;
 
 /* Text of the last error raised on the calling thread ("" if none); never NULL.
- * The pointer stays valid until the next call into the library on this thread. */
+ * The pointer stays valid until the next call into the library on this thread.
+ * Errors are reported this way instead of being printed before exit(1), the
+ * handling page "FlashMLA: 高性能GPU注意力机制计算库 文件结构分析" criticises
+ * in section "火辣点评：FlashMLA的类设计". */
 const char* mla_last_error(void);
 
 /* MLA_ABI_VERSION of the loaded library. */
@@ -139,10 +146,14 @@ mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
  * layer of a decode step.  Errors: INVALID_VALUE, UNSUPPORTED, HIP.
  */
 mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
-                            int num_parts, int32_t* sched, int32_t* split_offsets, void* stream);
+                            int num_parts, int32_t* sched, int32_t* split_offsets, hipStream_t stream);
 
 /*
- * Bytes of device workspace the decode entry points need: first the arrival
+ * Bytes of device workspace the decode entry points need.  The pieces a split
+ * request is cut into are merged by their LSE in a second kernel (page
+ * "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析", section
+ * "辅助优化：可编程依赖启动与瓦片调度": split-KV work, then a combine kernel),
+ * so each piece's fp32 output and LSE are parked here.  Layout: first the arrival
  * counters of mla_decode_fused (m_blocks * batch int32, rounded up to 256 bytes;
  * m_blocks = ceil(s_q*h_q / 64), or 1 when s_q*h_q <= 16), then fp32 partial
  * outputs and LSEs for up to (batch + num_parts) request pieces of s_q*h_q
@@ -184,7 +195,12 @@ typedef struct {
 
 /*
  * Paged MLA decode: mla_decode_splitkv followed by mla_decode_combine on
- * `stream`.  Writes out and lse for every (b, i, h).
+ * `stream`.  Writes out and lse for every (b, i, h), the attention defined at
+ * the top of this header (page "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析",
+ * sections "跷跷板调度的数学重构" for the online softmax and "辅助优化：可编程依赖
+ * 启动与瓦片调度" for the split-KV + combine structure; page "FlashAttention终极指南：
+ * 如何通过动态计算图实现3倍推理加速", section "核心代码实现解析", for the
+ * q / k_cache / block_table / cache_seqlens / softmax_scale / causal arguments).
  * An fp8 cache (kv_dtype = MLA_KV_FP8_E4M3) needs dtype bf16 and s_q*h_q <= 16
  * (UNSUPPORTED otherwise); k_cache is then 8-byte aligned instead of 16.
  * Alignment: q, k_cache, out must be 16-byte aligned, as must every stride
@@ -194,7 +210,7 @@ typedef struct {
  * alignment, non-finite or non-positive scale), UNSUPPORTED (dims, page size,
  * h_kv, dtype), WORKSPACE_TOO_SMALL, HIP (launch failed).
  */
-mla_status mla_decode(const mla_decode_args* args, void* stream);
+mla_status mla_decode(const mla_decode_args* args, hipStream_t stream);
 
 /*
  * First phase only: the split-KV attention kernel.  Requests handled by a single
@@ -204,7 +220,7 @@ mla_status mla_decode(const mla_decode_args* args, void* stream);
  * "辅助优化：可编程依赖启动与瓦片调度": the splitkv_mla kernel.)
  * Same arguments and errors as mla_decode.
  */
-mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream);
+mla_status mla_decode_splitkv(const mla_decode_args* args, hipStream_t stream);
 
 /*
  * Second phase only: merge the pieces of every split request by their LSE
@@ -214,7 +230,7 @@ mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream);
  * stream.  (Same page and section: the combine kernel.)
  * Same arguments and errors as mla_decode.
  */
-mla_status mla_decode_combine(const mla_decode_args* args, void* stream);
+mla_status mla_decode_combine(const mla_decode_args* args, hipStream_t stream);
 
 /*
  * Paged MLA decode with the combine folded into the split-KV kernel (the
@@ -234,7 +250,7 @@ mla_status mla_decode_combine(const mla_decode_args* args, void* stream);
  * read or write the counters.
  * Errors: as mla_decode.
  */
-mla_status mla_decode_fused(const mla_decode_args* args, void* stream);
+mla_status mla_decode_fused(const mla_decode_args* args, hipStream_t stream);
 
 /* Arguments of mla_merge_partials.  Strides are in ELEMENTS; the innermost
  * (feature) dimension of part_out and out must be contiguous. */
@@ -272,7 +288,7 @@ typedef struct {
  * Errors: INVALID_VALUE (null pointer, non-positive size, bad stride or
  * alignment), UNSUPPORTED (dtype), HIP (launch failed).
  */
-mla_status mla_merge_partials(const mla_merge_args* args, void* stream);
+mla_status mla_merge_partials(const mla_merge_args* args, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -159,7 +159,7 @@ mla_status mha_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
 }
 
 mla_status mha_get_metadata(const int32_t* cache_seqlens, int batch, int h_kv, int num_parts, int32_t* sched,
-                            int32_t* split_offsets, void* stream) {
+                            int32_t* split_offsets, hipStream_t stream) {
   if (batch <= 0 || h_kv <= 0) return fail(MLA_ERROR_INVALID_VALUE, "batch and h_kv must be positive");
   if ((long long)batch * h_kv > 2147483647LL / 8) return fail(MLA_ERROR_INVALID_VALUE, "batch*h_kv too large");
   if (num_parts <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_parts must be positive");
@@ -167,7 +167,7 @@ mla_status mha_get_metadata(const int32_t* cache_seqlens, int batch, int h_kv, i
   if (!aligned(cache_seqlens, 4) || !aligned(sched, 4) || !aligned(split_offsets, 4))
     return fail(MLA_ERROR_INVALID_VALUE, "int32 arrays must be 4-byte aligned");
   hipError_t e = mla::launch_metadata(cache_seqlens, batch * h_kv, h_kv, num_parts, MLA_FIXED_OVERHEAD, sched,
-                                      split_offsets, static_cast<hipStream_t>(stream));
+                                      split_offsets, stream);
   if (e != hipSuccess) return hip_fail(e, "metadata launch");
   return ok();
 }
@@ -181,25 +181,25 @@ mla_status mha_workspace_size(int batch, int s_q, int h_q, int h_kv, int head_di
   return ok();
 }
 
-mla_status mha_decode_splitkv(const mha_decode_args* args, void* stream) {
+mla_status mha_decode_splitkv(const mha_decode_args* args, hipStream_t stream) {
   mla_status st = check_mha(args);
   if (st != MLA_SUCCESS) return st;
   hipError_t e = mla::launch_mha_splitkv(make_mha_params(args), args->dtype, args->head_dim,
-                                         static_cast<hipStream_t>(stream));
+                                         stream);
   if (e != hipSuccess) return hip_fail(e, "MHA split-KV launch");
   return ok();
 }
 
-mla_status mha_decode_combine(const mha_decode_args* args, void* stream) {
+mla_status mha_decode_combine(const mha_decode_args* args, hipStream_t stream) {
   mla_status st = check_mha(args);
   if (st != MLA_SUCCESS) return st;
   hipError_t e = mla::launch_mha_combine(make_mha_params(args), args->dtype, args->head_dim,
-                                         static_cast<hipStream_t>(stream));
+                                         stream);
   if (e != hipSuccess) return hip_fail(e, "MHA combine launch");
   return ok();
 }
 
-mla_status mha_decode(const mha_decode_args* args, void* stream) {
+mla_status mha_decode(const mha_decode_args* args, hipStream_t stream) {
   mla_status st = mha_decode_splitkv(args, stream);
   if (st != MLA_SUCCESS) return st;
   return mha_decode_combine(args, stream);

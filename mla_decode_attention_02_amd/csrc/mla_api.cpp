@@ -205,7 +205,7 @@ mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
 }
 
 mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
-                            int num_parts, int32_t* sched, int32_t* split_offsets, void* stream) {
+                            int num_parts, int32_t* sched, int32_t* split_offsets, hipStream_t stream) {
   mla_status st = check_shape(batch, s_q, h_q, h_kv);
   if (st != MLA_SUCCESS) return st;
   if (num_parts <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_parts must be positive");
@@ -213,7 +213,7 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, in
   if (!aligned(cache_seqlens, 4) || !aligned(sched, 4) || !aligned(split_offsets, 4))
     return fail(MLA_ERROR_INVALID_VALUE, "int32 arrays must be 4-byte aligned");
   hipError_t e = mla::launch_metadata(cache_seqlens, batch, 1, num_parts, MLA_FIXED_OVERHEAD, sched,
-                                      split_offsets, static_cast<hipStream_t>(stream));
+                                      split_offsets, stream);
   if (e != hipSuccess) return hip_fail(e, "metadata launch");
   return ok();
 }
@@ -229,43 +229,43 @@ mla_status mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t
 
 namespace {
 
-mla_status launch_splitkv(const mla_decode_args* args, const mla::DecodeParams& p, void* stream) {
+mla_status launch_splitkv(const mla_decode_args* args, const mla::DecodeParams& p, hipStream_t stream) {
   const int tile = tile_rows(p.rows);
   const int m_blocks = (p.rows + tile - 1) / tile;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipStream_t hs = stream;
   hipError_t e = tile == 16 ? mla::launch_splitkv_narrow(p, args->dtype, hs)
                             : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
   if (e != hipSuccess) return hip_fail(e, "split-KV launch");
   return ok();
 }
 
-mla_status launch_combine(const mla_decode_args* args, const mla::DecodeParams& p, void* stream) {
-  hipError_t e = mla::launch_combine(p, args->dtype, static_cast<hipStream_t>(stream));
+mla_status launch_combine(const mla_decode_args* args, const mla::DecodeParams& p, hipStream_t stream) {
+  hipError_t e = mla::launch_combine(p, args->dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }
 
 }  // namespace
 
-mla_status mla_decode_splitkv(const mla_decode_args* args, void* stream) {
+mla_status mla_decode_splitkv(const mla_decode_args* args, hipStream_t stream) {
   mla_status st = check_decode(args);
   if (st != MLA_SUCCESS) return st;
   return launch_splitkv(args, make_params(args), stream);
 }
 
-mla_status mla_decode_combine(const mla_decode_args* args, void* stream) {
+mla_status mla_decode_combine(const mla_decode_args* args, hipStream_t stream) {
   mla_status st = check_decode(args);
   if (st != MLA_SUCCESS) return st;
   return launch_combine(args, make_params(args), stream);
 }
 
-mla_status mla_decode(const mla_decode_args* args, void* stream) {
+mla_status mla_decode(const mla_decode_args* args, hipStream_t stream) {
   mla_status st = mla_decode_splitkv(args, stream);
   if (st != MLA_SUCCESS) return st;
   return mla_decode_combine(args, stream);
 }
 
-mla_status mla_merge_partials(const mla_merge_args* a, void* stream) {
+mla_status mla_merge_partials(const mla_merge_args* a, hipStream_t stream) {
   if (!a) return fail(MLA_ERROR_INVALID_VALUE, "args is NULL");
   if (a->dtype != MLA_DTYPE_BF16 && a->dtype != MLA_DTYPE_FP16)
     return fail(MLA_ERROR_UNSUPPORTED, "dtype %d is not bf16 (0) or fp16 (1)", a->dtype);
@@ -303,12 +303,12 @@ mla_status mla_merge_partials(const mla_merge_args* a, void* stream) {
   m.out = a->out;
   m.o_s0 = a->out_stride[0]; m.o_s1 = a->out_stride[1]; m.o_s2 = a->out_stride[2];
   m.lse = a->lse;
-  hipError_t e = mla::launch_merge(m, a->dtype, static_cast<hipStream_t>(stream));
+  hipError_t e = mla::launch_merge(m, a->dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
 }
 
-mla_status mla_decode_fused(const mla_decode_args* args, void* stream) {
+mla_status mla_decode_fused(const mla_decode_args* args, hipStream_t stream) {
   mla_status st = check_decode(args);
   if (st != MLA_SUCCESS) return st;
   mla::DecodeParams p = make_params(args);
