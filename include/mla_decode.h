@@ -252,6 +252,25 @@ mla_status mla_decode_combine(const mla_decode_args* args, hipStream_t stream);
  */
 mla_status mla_decode_fused(const mla_decode_args* args, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mla_decode
+ * with its workspace taken from a static array of MLA_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every GPU it runs on until the process ends.
+ * args->workspace and args->workspace_bytes are ignored; every other argument,
+ * the result and the errors are those of mla_decode, and WORKSPACE_TOO_SMALL
+ * is returned (nothing enqueued) when mla_workspace_size(batch, s_q, h_q,
+ * num_parts) exceeds MLA_NOALLOC_SCRATCH_BYTES.  The call allocates nothing.
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress); make it outside graph capture.  All calls on one GPU
+ * share its array and it keeps the last call's contents (nothing in it has to
+ * start at zero): calls that overlap in time on one GPU -- on different
+ * streams, or from threads that do not order them -- race and may return
+ * wrong results.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status mla_decode_noalloc(const mla_decode_args* args, hipStream_t stream);
+
 /* Arguments of mla_merge_partials.  Strides are in ELEMENTS; the innermost
  * (feature) dimension of part_out and out must be contiguous. */
 typedef struct {

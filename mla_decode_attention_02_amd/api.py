@@ -111,7 +111,8 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.mla_get_metadata.argtypes = [p, i, i, i, i, i, p, p, p]
     L.mla_workspace_size.restype = st
     L.mla_workspace_size.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
-    for name in ("mla_decode", "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused"):
+    for name in ("mla_decode", "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused",
+                 "mla_decode_noalloc"):
         fn = getattr(L, name)
         fn.restype = st
         fn.argtypes = [ctypes.POINTER(DecodeArgs), p]
@@ -210,8 +211,8 @@ def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, s
     a.num_parts = sched.shape[0]
     a.softmax_scale = float(softmax_scale)
     a.causal = 1 if causal else 0
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a.out = out.data_ptr()
     a.out_stride[:] = list(out.stride()[:3])
     a.lse = lse.data_ptr()
@@ -339,6 +340,32 @@ def mla_decode_combine(q, k_cache, block_table, cache_seqlens, softmax_scale, ca
     """Second phase only (merge of split pieces)."""
     return _call("mla_decode_combine", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
                  metadata, buffers, k_scale)
+
+
+def mla_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                       cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
+                       metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode with the library's static per-GPU workspace: no workspace
+    tensor, and the C call allocates nothing (pass `out`/`lse` and `metadata`
+    to keep this function from allocating them).  Calls that overlap in time
+    on one GPU share that workspace and race."""
+    _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale)
+    if metadata is None:
+        metadata = get_metadata(cache_seqlens, q.shape[1], q.shape[2], k_cache.shape[2])
+    sched, offs = metadata
+    _check_metadata(sched, offs, q.shape[0], q.device)
+    B, s_q, h_q, _ = q.shape
+    if out is None:
+        out = torch.empty((B, s_q, h_q, D_V), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+    _check_outputs(q, out, lse, D_V)
+    a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs, None, out, lse,
+                    k_scale)
+    _check(lib().mla_decode_noalloc(ctypes.byref(a), _stream_ptr(q.device)))
+    return out, lse
 
 
 def mla_merge_partials(part_out: torch.Tensor, part_lse: torch.Tensor,

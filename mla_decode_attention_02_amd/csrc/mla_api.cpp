@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/mla_decode.h"
@@ -18,6 +19,12 @@
 #include "mla_internal.h"
 
 static_assert(mla::kFusedMaxPieces == MLA_FUSED_MAX_PIECES, "fused-merge limit");
+
+// Workspace of mla_decode_noalloc: one copy on every GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not the device array: kernels only ever see the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace mla {
 namespace api {
@@ -306,6 +313,64 @@ mla_status mla_merge_partials(const mla_merge_args* a, hipStream_t stream) {
   hipError_t e = mla::launch_merge(m, a->dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// This device's copy of `scratch`, looked up on the first call on the device.
+mla_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERROR_UNSUPPORTED, "device %d is beyond the %d devices mla_decode_noalloc serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static workspace");
+    if (!ptr) return fail(MLA_ERROR_HIP, "hipGetSymbolAddress returned NULL for the static workspace");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_SUCCESS;
+}
+
+}  // namespace
+
+mla_status mla_decode_noalloc(const mla_decode_args* args, hipStream_t stream) {
+  if (!args) return fail(MLA_ERROR_INVALID_VALUE, "args is NULL");
+  mla_status st = check_shape(args->batch, args->s_q, args->h_q, args->h_kv);
+  if (st != MLA_SUCCESS) return st;
+  if (args->num_parts <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_parts must be positive");
+  const size_t need = workspace_bytes(args->batch, args->s_q, args->h_q, args->num_parts);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERROR_WORKSPACE_TOO_SMALL,
+                "batch %d, s_q*h_q %d and num_parts %d need %zu bytes of workspace; the static workspace of "
+                "mla_decode_noalloc holds %zu (use mla_decode with a caller workspace)",
+                args->batch, args->s_q * args->h_q, args->num_parts, need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  // the host checks of mla_decode, against a placeholder for the workspace
+  // (replaced by the device array below), before any HIP call
+  mla_decode_args a = *args;
+  a.workspace = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  a.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  st = check_decode(&a);
+  if (st != MLA_SUCCESS) return st;
+  void* ptr = nullptr;
+  st = scratch_on_current_device(&ptr);
+  if (st != MLA_SUCCESS) return st;
+  a.workspace = ptr;
+  // the split-KV + combine pair of mla_decode: partial outputs only, no
+  // counters (those belong to the fused path), nothing to clear first
+  const mla::DecodeParams p = make_params(&a);
+  st = launch_splitkv(&a, p, stream);
+  if (st != MLA_SUCCESS) return st;
+  return launch_combine(&a, p, stream);
 }
 
 mla_status mla_decode_fused(const mla_decode_args* args, hipStream_t stream) {

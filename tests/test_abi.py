@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mla_last_error", "mla_abi_version", "mla_get_metadata_shape", "mla_get_metadata",
               "mla_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
-              "mla_decode_fused", "mla_merge_partials", "mha_get_metadata_shape", "mha_get_metadata",
+              "mla_decode_fused", "mla_decode_noalloc", "mla_merge_partials", "mha_get_metadata_shape",
+              "mha_get_metadata",
               "mha_workspace_size", "mha_decode", "mha_decode_splitkv", "mha_decode_combine"):
         assert n in names
 
@@ -166,6 +167,27 @@ def test_decode_rejects_bad_arguments(L, entry, name, brk, status):
     st = getattr(L, entry)(ctypes.byref(a), None)
     assert st == status, (name, L.mla_last_error().decode())
     assert L.mla_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("name,brk,status", [b for b in BREAKS if not b[0].startswith("workspace")],
+                         ids=[b[0] for b in BREAKS if not b[0].startswith("workspace")])
+def test_noalloc_rejects_bad_arguments(L, name, brk, status):
+    # the host checks of mla_decode, before the static workspace is looked up
+    # (workspace and workspace_bytes are ignored by this entry point)
+    a = _valid_args()
+    a.workspace, a.workspace_bytes = None, 0
+    brk(a)
+    st = L.mla_decode_noalloc(ctypes.byref(a), None)
+    assert st == status, (name, L.mla_last_error().decode())
+    assert L.mla_last_error().decode() != ""
+
+
+def test_noalloc_refuses_a_workspace_beyond_its_static_array(L):
+    a = _valid_args()
+    a.batch, a.s_q, a.h_q, a.num_parts = 64, 1, 128, 256      # (64 + 256) * 128 * 513 * 4 B > 64 MiB
+    assert L.mla_decode_noalloc(ctypes.byref(a), None) == WS_SMALL
+    assert "static workspace" in L.mla_last_error().decode()
+    assert L.mla_decode_noalloc(None, None) == INVALID
 
 
 def test_null_args_pointer(L):
