@@ -37,7 +37,7 @@
  * block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages);
  * `sched` / `split_offsets` come from mha_get_metadata with the same
  * cache_seqlens, h_kv and num_parts; the schedule cost
- * h_kv * sum_b (ceil(cache_seqlens[b] / 64) + 5) is below 2^31.
+ * h_kv * sum_b (ceil(cache_seqlens[b] / 64) + MLA_FIXED_OVERHEAD) is below 2^31.
  */
 #ifndef MHA_DECODE_H
 #define MHA_DECODE_H

@@ -42,7 +42,8 @@
  *    block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages);
  *    `sched` / `split_offsets` were produced by mla_get_metadata from the same
  *    cache_seqlens with the same num_parts; cache contents are finite; the total
- *    schedule cost sum_b (ceil(cache_seqlens[b] / 64) + 5) is below 2^31.
+ *    schedule cost sum_b (ceil(cache_seqlens[b] / 64) + MLA_FIXED_OVERHEAD) is
+ *    below 2^31.
  *  - Thread safety: all entry points may be called concurrently; the error
  *    text is kept per thread.
  */
@@ -66,7 +67,9 @@ typedef struct ihipStream_t* hipStream_t;
 #define MLA_D_V 512             /* value width: the first 512 columns       */
 #define MLA_PAGE_SIZE 64        /* tokens per KV-cache page                 */
 #define MLA_SCHED_FIELDS 8      /* int32 per scheduler partition            */
-#define MLA_FIXED_OVERHEAD 5    /* per-piece overhead, in pages (scheduler) */
+#define MLA_FIXED_OVERHEAD 2    /* per-piece overhead, in pages (scheduler):  */
+                                /* a piece's set-up and merge cost about two    */
+                                /* pages of attention on MI355X                 */
 #define MLA_FUSED_MAX_PIECES 4  /* mla_decode_fused merges requests cut into */
                                 /* at most this many pieces in its first kernel */
 

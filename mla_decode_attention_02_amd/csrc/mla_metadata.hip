@@ -76,36 +76,51 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
   // start positions: LDS when they fit, else split_offsets (overwritten at the end)
   int* C = batch <= kMetaLdsBatch ? start_s : split_offsets;
 
+  // each thread parks the costs of its own requests in C, then turns them
+  // into start positions in place: the lengths are read from memory once
   int local = 0;
   for (int b = lo; b < hi; ++b) {
     const int p = pages_of(seqlens[b / rep]);
-    local += p > 0 ? p + F : 0;
+    const int c = p > 0 ? p + F : 0;
+    C[b] = c;
+    local += c;
   }
   int total;
   const int first = block_exclusive_scan(local, scan_s, total);
   {
     int run = first;
     for (int b = lo; b < hi; ++b) {
+      const int c = C[b];
       C[b] = run;
-      const int p = pages_of(seqlens[b / rep]);
-      run += p > 0 ? p + F : 0;
+      run += c;
     }
     if (tid == 0) C[batch] = total;
   }
   __syncthreads();
   const int width = total > 0 ? (total + num_parts - 1) / num_parts : 1;
 
-  // pieces per request: how many partitions its page positions touch
-  auto pieces = [&](int start, int p) {
+  // pieces per request: how many partitions its page positions touch.  While
+  // C sits in LDS the lengths are not read again: a request costs
+  // C[b+1] - C[b], its pages are that less F (empty requests cost 0).  With C
+  // staged in split_offsets the last loop below overwrites it, so the lengths
+  // are read again there.
+  const bool c_in_lds = batch <= kMetaLdsBatch;
+  auto cost_at = [&](int b) {
+    if (c_in_lds) return C[b + 1] - C[b];
+    const int p = pages_of(seqlens[b / rep]);
+    return p > 0 ? p + F : 0;
+  };
+  auto pieces = [&](int start, int cost) {
+    const int p = cost > 0 ? cost - F : 0;
     return p > 0 ? (start + F + p - 1) / width - (start + F) / width + 1 : 0;
   };
   int nsum = 0;
   {
     int run = first;
     for (int b = lo; b < hi; ++b) {
-      const int p = pages_of(seqlens[b / rep]);
-      nsum += pieces(run, p);
-      run += p > 0 ? p + F : 0;
+      const int c = cost_at(b);
+      nsum += pieces(run, c);
+      run += c;
     }
   }
 
@@ -141,10 +156,10 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t* _
   {
     int run = sfirst, start = first;
     for (int b = lo; b < hi; ++b) {
-      const int p = pages_of(seqlens[b / rep]);
+      const int c = cost_at(b);        // C in LDS, or the length: never the entry overwritten here
       split_offsets[b] = run;
-      run += pieces(start, p);
-      start += p > 0 ? p + F : 0;
+      run += pieces(start, c);
+      start += c;
     }
     if (tid == 0) split_offsets[batch] = nall;
   }
