@@ -34,7 +34,9 @@
  *
  * Preconditions NOT checked on the host (undefined behaviour otherwise):
  * 0 <= cache_seqlens[b] <= max_pages_per_seq * 64; the entries
- * block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages);
+ * block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages)
+ * (both checked on the device by mla_check_paged_inputs, and by
+ * mha_decode_splitkv / mha_decode when MLA_DEBUG is set);
  * `sched` / `split_offsets` come from mha_get_metadata with the same
  * cache_seqlens, h_kv and num_parts; the schedule cost
  * h_kv * sum_b (ceil(cache_seqlens[b] / 64) + MLA_FIXED_OVERHEAD) is below 2^31.

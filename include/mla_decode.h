@@ -39,7 +39,9 @@
  *    it.  The process is never terminated.
  *  - Preconditions NOT checked on the host (violating them is undefined
  *    behaviour): 0 <= cache_seqlens[b] <= max_pages_per_seq * 64; the entries
- *    block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages);
+ *    block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages)
+ *    (these two are checked on the device by mla_check_paged_inputs, and by
+ *    every decode entry point when the environment variable MLA_DEBUG is set);
  *    `sched` / `split_offsets` were produced by mla_get_metadata from the same
  *    cache_seqlens with the same num_parts; cache contents are finite; the total
  *    schedule cost sum_b (ceil(cache_seqlens[b] / 64) + MLA_FIXED_OVERHEAD) is
@@ -273,6 +275,28 @@ mla_status mla_decode_fused(const mla_decode_args* args, hipStream_t stream);
  */
 #define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 mla_status mla_decode_noalloc(const mla_decode_args* args, hipStream_t stream);
+
+/*
+ * Debug check of the paged-cache indices on the device: every length
+ * cache_seqlens[b] must lie in [0, 64 * max_pages_per_seq] and every entry
+ * block_table[b, j] with j < ceil(cache_seqlens[b] / 64) in [0, num_pages);
+ * entries past a request's last page are not read.  block_table is device
+ * int32 [batch, bt_stride >= max_pages_per_seq], cache_seqlens device int32
+ * [batch].  The call runs two small kernels on `stream`, then waits for the
+ * stream (so it cannot be captured into a graph) and returns
+ * MLA_ERROR_INVALID_VALUE, with the first bad entry (lowest request, then
+ * column; a bad length before its columns) named in mla_last_error(), or
+ * MLA_SUCCESS.  The result lives in a static per-GPU word: calls serialise on
+ * a process-wide lock.  When the environment variable MLA_DEBUG is set (to
+ * anything but "" or "0"), mla_decode, mla_decode_splitkv, mla_decode_fused,
+ * mla_decode_noalloc and mha_decode_splitkv run this check after their host
+ * checks and return its error without launching.  Bad indices are reported as
+ * a status, not by ending the process: the print-and-exit(1) handling is what
+ * page "FlashMLA: 高性能GPU注意力机制计算库 文件结构分析", section
+ * "火辣点评：FlashMLA的类设计", criticises.
+ */
+mla_status mla_check_paged_inputs(const int32_t* block_table, int64_t bt_stride, const int32_t* cache_seqlens,
+                                  int batch, int max_pages_per_seq, int num_pages, hipStream_t stream);
 
 /* Arguments of mla_merge_partials.  Strides are in ELEMENTS; the innermost
  * (feature) dimension of part_out and out must be contiguous. */

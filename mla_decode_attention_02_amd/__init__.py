@@ -10,7 +10,7 @@ and raises if the library has not been built.
 __all__ = ["get_metadata", "get_metadata_shape", "workspace_size", "mla_decode",
            "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused", "mla_merge_partials",
            "mha_get_metadata", "mha_get_metadata_shape", "mha_workspace_size", "mha_decode",
-           "mha_decode_splitkv", "mha_decode_combine", "library_path"]
+           "mha_decode_splitkv", "mha_decode_combine", "mla_decode_noalloc", "check_paged_inputs", "library_path"]
 
 
 def __getattr__(name):

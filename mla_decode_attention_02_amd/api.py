@@ -118,6 +118,8 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
         fn.argtypes = [ctypes.POINTER(DecodeArgs), p]
     L.mla_merge_partials.restype = st
     L.mla_merge_partials.argtypes = [ctypes.POINTER(MergeArgs), p]
+    L.mla_check_paged_inputs.restype = st
+    L.mla_check_paged_inputs.argtypes = [p, ctypes.c_int64, p, i, i, i, p]
     L.mha_get_metadata_shape.restype = st
     L.mha_get_metadata_shape.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
     L.mha_get_metadata.restype = st
@@ -182,6 +184,26 @@ def get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int = 1,
     _check(lib().mla_get_metadata(seq.data_ptr(), batch, s_q, h_q, h_kv, num_parts,
                                   sched.data_ptr(), offs.data_ptr(), _stream_ptr(seq.device)))
     return sched, offs
+
+
+def check_paged_inputs(block_table: torch.Tensor, cache_seqlens: torch.Tensor, num_pages: int) -> None:
+    """Check on the device that every length lies in [0, 64 * columns of
+    block_table] and every block_table entry a request reads lies in
+    [0, num_pages); raises MlaError naming the first bad entry.  Waits for the
+    current stream.  Setting MLA_DEBUG=1 in the environment makes every decode
+    call run the same check first."""
+    if block_table.dtype != torch.int32 or not block_table.is_cuda or block_table.dim() != 2:
+        raise ValueError("block_table must be a 2-D int32 device tensor")
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.dim() != 1:
+        raise ValueError("cache_seqlens must be a 1-D int32 device tensor")
+    if block_table.stride(1) != 1 or not cache_seqlens.is_contiguous():
+        raise ValueError("block_table rows and cache_seqlens must be contiguous")
+    if block_table.shape[0] != cache_seqlens.shape[0] or cache_seqlens.device != block_table.device:
+        raise ValueError("block_table and cache_seqlens must have the same batch and device")
+    with torch.cuda.device(block_table.device):
+        _check(lib().mla_check_paged_inputs(block_table.data_ptr(), block_table.stride(0), cache_seqlens.data_ptr(),
+                                            block_table.shape[0], block_table.shape[1], num_pages,
+                                            _stream_ptr(block_table.device)))
 
 
 def workspace_size(batch: int, s_q: int, h_q: int, num_parts: int) -> int:

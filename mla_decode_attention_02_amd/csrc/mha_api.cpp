@@ -183,6 +183,9 @@ mla_status mha_workspace_size(int batch, int s_q, int h_q, int h_kv, int head_di
 
 mla_status mha_decode_splitkv(const mha_decode_args* args, hipStream_t stream) {
   mla_status st = check_mha(args);
+  if (st == MLA_SUCCESS && mla::debug_checks_enabled())
+    st = mla::check_paged_inputs(args->block_table, args->bt_stride, args->cache_seqlens, args->batch,
+                                 args->max_pages_per_seq, args->num_pages, stream);
   if (st != MLA_SUCCESS) return st;
   hipError_t e = mla::launch_mha_splitkv(make_mha_params(args), args->dtype, args->head_dim,
                                          stream);

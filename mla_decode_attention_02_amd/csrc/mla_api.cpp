@@ -252,10 +252,18 @@ mla_status launch_combine(const mla_decode_args* args, const mla::DecodeParams& 
   return ok();
 }
 
+// With MLA_DEBUG set: the device check of the paged-cache indices.
+mla_status debug_check(const mla_decode_args* a, hipStream_t stream) {
+  if (!mla::debug_checks_enabled()) return MLA_SUCCESS;
+  return mla::check_paged_inputs(a->block_table, a->bt_stride, a->cache_seqlens, a->batch, a->max_pages_per_seq,
+                                 a->num_pages, stream);
+}
+
 }  // namespace
 
 mla_status mla_decode_splitkv(const mla_decode_args* args, hipStream_t stream) {
   mla_status st = check_decode(args);
+  if (st == MLA_SUCCESS) st = debug_check(args, stream);
   if (st != MLA_SUCCESS) return st;
   return launch_splitkv(args, make_params(args), stream);
 }
@@ -360,6 +368,7 @@ mla_status mla_decode_noalloc(const mla_decode_args* args, hipStream_t stream) {
   a.workspace = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
   a.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
   st = check_decode(&a);
+  if (st == MLA_SUCCESS) st = debug_check(&a, stream);
   if (st != MLA_SUCCESS) return st;
   void* ptr = nullptr;
   st = scratch_on_current_device(&ptr);
@@ -375,6 +384,7 @@ mla_status mla_decode_noalloc(const mla_decode_args* args, hipStream_t stream) {
 
 mla_status mla_decode_fused(const mla_decode_args* args, hipStream_t stream) {
   mla_status st = check_decode(args);
+  if (st == MLA_SUCCESS) st = debug_check(args, stream);
   if (st != MLA_SUCCESS) return st;
   mla::DecodeParams p = make_params(args);
   p.fuse_max = mla::kFusedMaxPieces;

@@ -24,4 +24,14 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace api
+
+// True when the environment variable MLA_DEBUG is set to anything but "" or
+// "0": the decode entry points then check the paged-cache indices on the
+// device before launching (synchronous, so not for graph capture).
+bool debug_checks_enabled();
+// The device check of block_table and cache_seqlens (mla_check.hip): waits
+// for `stream`; MLA_ERROR_INVALID_VALUE naming the first bad entry.  Leaves
+// the error text alone on success.
+mla_status check_paged_inputs(const int32_t* block_table, int64_t bt_stride, const int32_t* seqlens, int batch,
+                              int max_pages, int num_pages, hipStream_t stream);
 }  // namespace mla

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mla_last_error", "mla_abi_version", "mla_get_metadata_shape", "mla_get_metadata",
               "mla_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
-              "mla_decode_fused", "mla_decode_noalloc", "mla_merge_partials", "mha_get_metadata_shape",
+              "mla_decode_fused", "mla_decode_noalloc", "mla_check_paged_inputs", "mla_merge_partials",
+              "mha_get_metadata_shape",
               "mha_get_metadata",
               "mha_workspace_size", "mha_decode", "mha_decode_splitkv", "mha_decode_combine"):
         assert n in names
@@ -188,6 +189,22 @@ def test_noalloc_refuses_a_workspace_beyond_its_static_array(L):
     assert L.mla_decode_noalloc(ctypes.byref(a), None) == WS_SMALL
     assert "static workspace" in L.mla_last_error().decode()
     assert L.mla_decode_noalloc(None, None) == INVALID
+
+
+@pytest.mark.parametrize("bt,bt_stride,sl,batch,width,pages,what", [
+    (0, 8, 1 << 21, 2, 8, 10, "NULL"),
+    (1 << 20, 8, 0, 2, 8, 10, "NULL"),
+    ((1 << 20) + 2, 8, 1 << 21, 2, 8, 10, "aligned"),
+    (1 << 20, 8, (1 << 21) + 1, 2, 8, 10, "aligned"),
+    (1 << 20, 8, 1 << 21, 0, 8, 10, "positive"),
+    (1 << 20, 8, 1 << 21, 2, 0, 10, "positive"),
+    (1 << 20, 8, 1 << 21, 2, 8, 0, "positive"),
+    (1 << 20, 7, 1 << 21, 2, 8, 10, "bt_stride"),
+], ids=["null_table", "null_lengths", "table_align", "lengths_align", "batch", "width", "pages", "stride"])
+def test_check_paged_inputs_rejects_before_launch(L, bt, bt_stride, sl, batch, width, pages, what):
+    # the fake addresses are never dereferenced: every case fails on the host
+    assert L.mla_check_paged_inputs(bt, bt_stride, sl, batch, width, pages, None) == INVALID
+    assert what in L.mla_last_error().decode()
 
 
 def test_null_args_pointer(L):
