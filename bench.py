@@ -49,7 +49,8 @@ CSRC = os.path.join(ROOT, "mla_decode_attention_02_amd", "csrc")
 KERNEL_SOURCES = {
     "splitkv_wide_kernel": ["mla_splitkv_wide.hip", "mla_splitkv.hpp", "mla_common.hpp"],
     "splitkv_narrow_kernel": ["mla_splitkv_narrow.hip", "mla_splitkv.hpp", "mla_common.hpp"],
-    "splitkv_fp8_kernel": ["mla_splitkv_fp8.hip", "mla_splitkv.hpp", "mla_common.hpp"],
+    "splitkv_fp8_kernel": ["mla_splitkv_fp8.hip", "mla_fp8.hpp", "mla_splitkv.hpp", "mla_common.hpp"],
+    "splitkv_wide_fp8_kernel": ["mla_splitkv_wide8.hip", "mla_fp8.hpp", "mla_splitkv.hpp", "mla_common.hpp"],
     "mha_splitkv_kernel": ["mha_decode.hip", "mla_common.hpp"],
     "mha_keysplit_kernel": ["mha_decode.hip", "mla_common.hpp"],
 }
@@ -58,7 +59,7 @@ KERNEL_SOURCES = {
 def mla_kernel_name(w) -> str:
     """The split-KV kernel that runs a workload."""
     if w.kv == "fp8":
-        return "splitkv_fp8_kernel"
+        return "splitkv_wide_fp8_kernel" if w.rows > 16 else "splitkv_fp8_kernel"
     return "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
 
 
@@ -105,6 +106,70 @@ def stored_traffic(kernel: str, workload_name: str):
 def _counter_rows(path):
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
+
+
+MFMA_PASS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+             "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"]
+LDS_PASS = ["SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH",
+            "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_LDS_DATA_FIFO_FULL", "GRBM_GUI_ACTIVE"]
+
+
+def pipe_counters(out_dir: str, tag: str, kernel: str):
+    """MFMA-pipe and LDS figures of one kernel from the two counter passes
+    (directories pmcm_<tag> and pmcl_<tag>), or None when they are absent.
+
+    GRBM_GUI_ACTIVE is summed over the XCDs, so the kernel's clock count is it
+    divided by the XCD count; SQ_VALU_MFMA_BUSY_CYCLES and SQ_LDS_IDX_ACTIVE are
+    summed over SIMDs and CUs.  Each SQ_INSTS_VALU_MFMA_MOPS_* unit is 512 FLOPs;
+    each SQ_INSTS_LDS_*_BANDWIDTH unit is 64 bytes."""
+    dirs = {k: os.path.join(out_dir, f"pmc{k}_{tag}") for k in ("m", "l")}
+    if not all(os.path.exists(os.path.join(d, "p_counter_collection.csv")) for d in dirs.values()):
+        return None
+    agent = [r for r in _counter_rows(os.path.join(dirs["m"], "p_agent_info.csv")) if r["Agent_Type"] == "GPU"][0]
+    n_xcc, n_cu, n_simd = int(agent["Num_Xcc"]), int(agent["Cu_Count"]), int(agent["Simd_Count"])
+
+    def sums(d):
+        tot, seen = {}, {}
+        for r in _counter_rows(os.path.join(d, "p_counter_collection.csv")):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            tot[r["Counter_Name"]] = tot.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            seen[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        return tot, len(seen), sum(seen.values())
+
+    m, nm, ns_m = sums(dirs["m"])
+    l, nl, _ = sums(dirs["l"])
+    clk_m = m["GRBM_GUI_ACTIVE"] / n_xcc
+    clk_l = l["GRBM_GUI_ACTIVE"] / n_xcc
+    flops = 512.0 * (m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + m["SQ_INSTS_VALU_MFMA_MOPS_F16"])
+    sclk = clk_m / (ns_m * 1e-9) / 1e6
+    rec = {
+        "dispatches": [nm, nl],
+        "sclk_mhz": round(sclk),
+        "mfma_busy_frac": round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (clk_m * n_simd), 4),
+        "mfma_tflops_per_dispatch": round(flops / nm / 1e12, 4),
+        "mfma_tflops_s": round(flops / (ns_m * 1e-9) / 1e12, 1),
+        "cu_busy_frac": round(m["SQ_BUSY_CU_CYCLES"] / (clk_m * n_cu), 4),
+        "wave_wait_frac": round(m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"], 4),
+        "lds_active_frac": round(l["SQ_LDS_IDX_ACTIVE"] / (clk_l * n_cu), 4),
+        "lds_load_bytes_per_clk_cu": round(64.0 * l["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / (clk_l * n_cu), 1),
+        "lds_store_bytes_per_clk_cu": round(64.0 * l["SQ_INSTS_LDS_STORE_BANDWIDTH"] / (clk_l * n_cu), 1),
+        "lds_bank_conflict_per_active": round(l["SQ_LDS_BANK_CONFLICT"] / max(l["SQ_LDS_IDX_ACTIVE"], 1.0), 4),
+        "lds_wait_frac": round(l["SQ_WAIT_INST_LDS"] / l["SQ_WAVE_CYCLES"], 4),
+    }
+    lines = ["", "MFMA pipe and LDS (two further counter passes; sums over the dispatches counted):", "",
+             f"- clock: GRBM_GUI_ACTIVE / {n_xcc} XCDs over the dispatch time = {rec['sclk_mhz']} MHz",
+             f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x {n_simd} SIMDs) = {rec['mfma_busy_frac']:.3f}",
+             f"- MFMA work: SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F16 = {rec['mfma_tflops_per_dispatch'] * 1e3:.2f} GFLOP "
+             f"per dispatch, {rec['mfma_tflops_s']:.0f} TFLOP/s over the dispatch time",
+             f"- CU busy: SQ_BUSY_CU_CYCLES / (clock cycles x {n_cu} CUs) = {rec['cu_busy_frac']:.3f}",
+             f"- waves waiting: SQ_WAIT_ANY / SQ_WAVE_CYCLES = {rec['wave_wait_frac']:.3f}",
+             f"- LDS active: SQ_LDS_IDX_ACTIVE / (clock cycles x {n_cu} CUs) = {rec['lds_active_frac']:.3f}",
+             f"- LDS reads: {rec['lds_load_bytes_per_clk_cu']:.1f} B per clock per CU; LDS stores "
+             f"{rec['lds_store_bytes_per_clk_cu']:.1f} B (LDS-DMA writes are not counted here)",
+             f"- bank conflicts: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = {rec['lds_bank_conflict_per_active']:.4f}",
+             f"- waves waiting on LDS: SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES = {rec['lds_wait_frac']:.3f}"]
+    return rec, lines
 
 
 def summarize_profiles(out_dir: str, workload: int) -> str:
@@ -166,6 +231,10 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
              f"python3 bench.py --calibrate-copy {COPY_MIB}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_copy -o p -- "
              f"python3 bench.py --calibrate-copy {COPY_MIB}",
+             f"rocprofv3 --pmc {' '.join(MFMA_PASS)} --output-format csv -d gpurun_out/pmcm_{tag} -o p -- "
+             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline",
+             f"rocprofv3 --pmc {' '.join(LDS_PASS)} --output-format csv -d gpurun_out/pmcl_{tag} -o p -- "
+             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline",
              f"python3 bench.py --summarize-profiles gpurun_out --workload {workload}",
              "```", "", "Kernel trace statistics (--stats):", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -181,7 +250,12 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
               f"- FETCH_SIZE {fetch_kib:.1f} KiB x {scale_f:.3f} = {fetch_kib * scale_f / 1024:.1f} MiB read",
               f"- WRITE_SIZE {write_kib:.1f} KiB x {scale_w:.3f} = {write_kib * scale_w / 1024:.1f} MiB written",
               f"- HBM traffic {hbm / 1e6:.1f} MB per launch against {alg / 1e6:.1f} MB algorithmic "
-              f"(ratio {hbm / alg:.2f})", "", "```json", json.dumps(rec), "```", ""]
+              f"(ratio {hbm / alg:.2f})"]
+    pipe = pipe_counters(out_dir, tag, kernel)
+    if pipe is not None:
+        rec["pipe"] = pipe[0]
+        lines += pipe[1]
+    lines += ["", "```json", json.dumps(rec), "```", ""]
     os.makedirs(PROFILES, exist_ok=True)
     path = profile_path(kernel, w.name)
     with open(path, "w") as f:

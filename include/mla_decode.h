@@ -206,8 +206,8 @@ typedef struct {
  * 启动与瓦片调度" for the split-KV + combine structure; page "FlashAttention终极指南：
  * 如何通过动态计算图实现3倍推理加速", section "核心代码实现解析", for the
  * q / k_cache / block_table / cache_seqlens / softmax_scale / causal arguments).
- * An fp8 cache (kv_dtype = MLA_KV_FP8_E4M3) needs dtype bf16 and s_q*h_q <= 16
- * (UNSUPPORTED otherwise); k_cache is then 8-byte aligned instead of 16.
+ * An fp8 cache (kv_dtype = MLA_KV_FP8_E4M3) needs dtype bf16 (UNSUPPORTED
+ * otherwise), for any s_q*h_q; k_cache is then 8-byte aligned instead of 16.
  * Alignment: q, k_cache, out must be 16-byte aligned, as must every stride
  * times the element size (q_stride[*], k_stride[0..1], out_stride[*] multiples
  * of 8); lse and the int32 arrays 4-byte aligned.

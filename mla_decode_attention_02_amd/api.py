@@ -330,7 +330,7 @@ def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor
     """Paged MLA decode.  Returns (out [B, s_q, h_q, 512] in q's dtype,
     lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result
     (computed here when omitted); `buffers` lets a caller reuse outputs.  An
-    fp8 cache (torch.float8_e4m3fn, with a bf16 q and s_q*h_q <= 16) takes an
+    fp8 cache (torch.float8_e4m3fn, with a bf16 q) takes an
     optional per-page fp32 scale `k_scale` [num_pages] (any finite value; the
     cached row is code * scale)."""
     return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,

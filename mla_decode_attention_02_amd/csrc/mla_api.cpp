@@ -107,8 +107,8 @@ mla_status check_decode(const mla_decode_args* a) {
   if (st != MLA_SUCCESS) return st;
   if (a->kv_dtype != MLA_KV_SAME && a->kv_dtype != MLA_KV_FP8_E4M3)
     return fail(MLA_ERROR_UNSUPPORTED, "kv_dtype %d is not MLA_KV_SAME (0) or MLA_KV_FP8_E4M3 (1)", a->kv_dtype);
-  if (a->kv_dtype == MLA_KV_FP8_E4M3 && (a->dtype != MLA_DTYPE_BF16 || (long long)a->s_q * a->h_q > 16))
-    return fail(MLA_ERROR_UNSUPPORTED, "an fp8 cache needs dtype bf16 and s_q*h_q <= 16");
+  if (a->kv_dtype == MLA_KV_FP8_E4M3 && a->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERROR_UNSUPPORTED, "an fp8 cache needs dtype bf16");
   if (a->k_scale && !aligned(a->k_scale, 4)) return fail(MLA_ERROR_INVALID_VALUE, "k_scale must be 4-byte aligned");
   if (a->num_pages <= 0 || a->max_pages_per_seq <= 0 || a->num_parts <= 0)
     return fail(MLA_ERROR_INVALID_VALUE, "num_pages, max_pages_per_seq and num_parts must be positive");
@@ -240,7 +240,8 @@ mla_status launch_splitkv(const mla_decode_args* args, const mla::DecodeParams& 
   const int tile = tile_rows(p.rows);
   const int m_blocks = (p.rows + tile - 1) / tile;
   hipStream_t hs = stream;
-  hipError_t e = tile == 16 ? mla::launch_splitkv_narrow(p, args->dtype, hs)
+  hipError_t e = tile == 16  ? mla::launch_splitkv_narrow(p, args->dtype, hs)
+                 : p.kv_fp8 ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
                             : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
   if (e != hipSuccess) return hip_fail(e, "split-KV launch");
   return ok();

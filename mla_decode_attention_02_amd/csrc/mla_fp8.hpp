@@ -1,0 +1,64 @@
+// Pieces shared by the split-KV kernels over an fp8 e4m3 cache (gfx950).
+//
+// The cache holds e4m3 codes and one fp32 scale per page (K = scale * code).
+// Pages stay codes in LDS and operands are converted to bf16 as they are read:
+// every e4m3 value is a bf16 value, so the conversion is exact (pages
+// "DeepSeek开源FlashMLA全解析：性能革命背后的技术密码", section "1.2 计算模式创新：
+// 混合精度矩阵乘法", and "云上AI推理新突破：FlashMLA赋能DeepSeek-V2-Lite提速16%",
+// section "3. 动态精度缩放", for fp8 keys with a scale and 16-bit softmax and
+// value products).
+//
+// LDS image of cached rows: row r at r * 576 bytes, 36 chunks of 16 bytes,
+// chunk c of row r at slot c ^ rot8(r), rot8(r) = 2 * (bit 2 of r xor bit 4
+// of r) (which stays inside the row's aligned group of four chunks), so that
+// the 16-byte score-operand reads of 16 rows and the transposed reads of 8
+// rows meet distinct bank groups.
+#pragma once
+
+#include "mla_splitkv.hpp"
+
+namespace mla {
+
+constexpr int kRow8 = kDK;                   // bytes of a cached row of codes
+constexpr int kPage8 = kPage * kRow8;        // 36864 bytes of a page image
+constexpr int kSlots8 = kPage8 / 16;         // 2304 sixteen-byte slots
+constexpr int kDma8 = kPage8 / 1024 / 4;     // LDS-DMA instructions per wave and page (9)
+
+__device__ __forceinline__ int rot8(int r) { return ((r >> 1) ^ (r >> 3)) & 2; }
+
+// Eight e4m3 codes (one 8-byte word) -> eight bf16 values.
+__device__ __forceinline__ u32x4 codes8_to_bf16(u32x2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+// Q fragments in the contraction order of the 16-byte K reads: fragment 2m
+// holds columns 64m + 16g .. +8 and fragment 2m + 1 columns 64m + 16g + 8 .. +8.
+__device__ __forceinline__ void load_q_frag8(const DecodeParams& p, int b, int row, int g, u32x4 (&qf)[18]) {
+  if (row < p.rows) {
+    const int tok = row / p.h_q;
+    const int head = row - tok * p.h_q;
+    const __bf16* base = (const __bf16*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2 + 16 * g;
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+      qf[2 * m] = *(const u32x4*)(base + 64 * m);
+      qf[2 * m + 1] = *(const u32x4*)(base + 64 * m + 8);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 18; ++k) qf[k] = u32x4{0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ u32x2 ld_lds_tr8(const MLA_LDS char* p) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS v2i*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace mla

@@ -21,6 +21,8 @@ hipError_t launch_splitkv_wide(const DecodeParams& p, int dtype, int m_blocks, h
 hipError_t launch_splitkv_narrow(const DecodeParams& p, int dtype, hipStream_t st);
 // The same over an fp8 e4m3 cache (bf16 q): grid (num_parts), 256 threads.
 hipError_t launch_splitkv_fp8(const DecodeParams& p, hipStream_t st);
+// 64-row tiles over an fp8 e4m3 cache (bf16 q): grid (num_parts, m_blocks), 512 threads.
+hipError_t launch_splitkv_wide_fp8(const DecodeParams& p, int m_blocks, hipStream_t st);
 // Merge of split pieces: grid (batch, ceil(rows / 4), 2 column halves), 256 threads.
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t st);
 // Merge of context-parallel shards: grid (batch, ceil(rows / 4)), 256 threads.

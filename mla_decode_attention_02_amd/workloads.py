@@ -70,7 +70,8 @@ class Workload:
 
 
 # The workloads the measurements are quoted on.  Seeds are the index, except
-# for 6: workload 3 (same seed, lengths and page table) with an fp8 cache.
+# for the fp8-cache variants 6, 11 and 12: workloads 3, 2 and 5 (same seed,
+# lengths and page table) with an fp8 cache.  (7..10 are the MHA workloads.)
 WORKLOADS = {
     1: Workload("tiny", 2, 1, 16, "bf16", 1.0, False, seqlens=(64, 100), seed=1,
                 description="B2 s_q1 h_q16 bf16, s_k {64,100}, non-causal"),
@@ -87,6 +88,12 @@ WORKLOADS = {
     6: Workload("varlen_bs128_hq16_fp8kv", 128, 1, 16, "bf16", 1.0, False, seqlen_range=(1, 8192), seed=3,
                 kv="fp8",
                 description="B128 s_q1 h_q16 bf16 q, fp8 e4m3 KV with per-page scales, s_k ~ U[1,8192]"),
+    11: Workload("bs64_hq128_sk4096_fp8kv", 64, 1, 128, "bf16", 1.0, False, seqlens=(4096,) * 64, seed=2,
+                 kv="fp8",
+                 description="B64 s_q1 h_q128 bf16 q, fp8 e4m3 KV with per-page scales, every s_k 4096"),
+    12: Workload("longctx_bs4_hq128_fp8kv", 4, 1, 128, "bf16", 1.0, False,
+                 seqlens=(65536, 98304, 131072, 131072), seed=5, kv="fp8",
+                 description="B4 s_q1 h_q128 bf16 q, fp8 e4m3 KV with per-page scales, s_k {64K,96K,128K,128K}"),
 }
 
 

@@ -153,7 +153,6 @@ BREAKS = [
     ("workspace small", lambda a: setattr(a, "workspace_bytes", 1024), WS_SMALL),
     ("kv_dtype", lambda a: setattr(a, "kv_dtype", 2), UNSUPPORTED),
     ("fp8 with fp16 q", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "dtype", 1)), UNSUPPORTED),
-    ("fp8 with 32 rows", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "h_q", 32)), UNSUPPORTED),
     ("fp8 k misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "k_cache", (1 << 21) + 4)), INVALID),
     ("k_scale misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "k_scale", 10 * (1 << 20) + 2)),
      INVALID),

@@ -66,11 +66,12 @@ def test_mha_counts():
 
 def test_kernel_attribution():
     # the split-KV kernel each workload runs, as the library dispatches it
-    # (16 rows or fewer: narrow; more: wide; fp8 cache: the fp8 kernel; MHA:
-    # key split for fp8 caches with small row tiles, else mha_splitkv_kernel)
-    assert [bench.mla_kernel_name(WORKLOADS[i]) for i in (1, 2, 3, 4, 5, 6)] == [
+    # (16 rows or fewer: narrow; more: wide; fp8 cache: the fp8 kernel of the
+    # same width; MHA: key split for fp8 caches with small row tiles, else
+    # mha_splitkv_kernel)
+    assert [bench.mla_kernel_name(WORKLOADS[i]) for i in (1, 2, 3, 4, 5, 6, 11, 12)] == [
         "splitkv_narrow_kernel", "splitkv_wide_kernel", "splitkv_narrow_kernel", "splitkv_wide_kernel",
-        "splitkv_wide_kernel", "splitkv_fp8_kernel"]
+        "splitkv_wide_kernel", "splitkv_fp8_kernel", "splitkv_wide_fp8_kernel", "splitkv_wide_fp8_kernel"]
     assert [bench.mha_kernel_name(MHA_WORKLOADS[i]) for i in (7, 8, 9, 10)] == [
         "mha_splitkv_kernel", "mha_splitkv_kernel", "mha_keysplit_kernel", "mha_splitkv_kernel"]
 

@@ -94,7 +94,7 @@ def test_metadata_bit_exact(seqlens, parts):
     assert np.array_equal(offs.cpu().numpy(), ref_o)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 11, 12])
 def test_metadata_workloads_bit_exact(idx):
     w = WORKLOADS[idx]
     seqlens = workload_seqlens(idx)
@@ -191,6 +191,13 @@ FP8_EDGE = [
     (1, 3, (300, 7), False, "amax", 5),
     (4, 4, (3, 200, 64), True, "pow2", 4),
     (1, 16, (2000, 1, 700), False, "amax", 9),
+    # more than 16 rows: 64-row tiles
+    (1, 128, (1, 63, 64, 65, 300), False, "amax", None),
+    (2, 64, (1, 2, 64, 129, 500), True, "pow2", 3),
+    (1, 32, (700, 5), False, "none", 4),
+    (1, 128, (2000,), False, "amax", 7),
+    (3, 40, (100, 1, 333), True, "amax", 2),
+    (1, 17, (129, 64, 31), False, "pow2", None),
 ]
 
 
@@ -207,26 +214,51 @@ def test_fp8_small_parity(s_q, h_q, seqlens, causal, mode, parts, entry):
     compare(out, lse, ref_o, ref_l, tag)
 
 
-def test_fp8_scale_is_applied_per_page():
+def range_tol(ref_o):
+    """Output bound when a page scale makes the outputs large: the bf16
+    rounding of the output and of the probabilities is 2^-8 relative each, on
+    values up to the largest output, so together about 2^-7 max|O|; TOL_O is
+    that for max|O| = 2, and the bound grows in proportion beyond it."""
+    return TOL_O * max(1.0, float(np.abs(ref_o).max()) / 2.0)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fp8_scale_is_applied_per_page(h_q):
     """One used page's scale is tripled: the result must follow the oracle, which
     a kernel that ignored the scale, or took another page's, would not (the
     two oracle results differ by several units).  That page's values, and so
     the outputs and their bf16 rounding step, grow up to threefold: the output
-    tolerance grows with them."""
-    _say("fp8 per-page scale")
-    x = make_inputs(2, 1, 16, "bf16", seqlens=(300, 129), seed=77, kv_dtype="fp8")
+    tolerance grows with the largest oracle output."""
+    _say(f"fp8 per-page scale h_q={h_q}")
+    x = make_inputs(2, 1, h_q, "bf16", seqlens=(300, 129), seed=77, kv_dtype="fp8")
     before, _ = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
     x.k_scale[int(x.block_table[0, 2])] *= 3.0
     out, lse, _ = run(x, 3)
     ref_o, ref_l = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
     assert np.abs(ref_o - before).max() > 1.0
-    compare(out, lse, ref_o, ref_l, "fp8 page scale x3", tol_o=3 * TOL_O)
+    compare(out, lse, ref_o, ref_l, "fp8 page scale x3", tol_o=range_tol(ref_o))
 
 
-def test_fp8_unused_slots_and_pages_are_never_read_bitwise():
-    _say("fp8: garbage codes in unused slots, NaN codes in unused pages")
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fp8_negative_and_zero_scales(h_q):
+    """Any finite scale is allowed: one page's scale made negative (its keys
+    and values change sign), another's zero (its keys score 0 and its values
+    vanish)."""
+    _say(f"fp8 negative and zero scales h_q={h_q}")
+    x = make_inputs(3, 1, h_q, "bf16", seqlens=(300, 129, 64), seed=78, kv_dtype="fp8")
+    x.k_scale[int(x.block_table[0, 1])] *= -1.5
+    x.k_scale[int(x.block_table[1, 0])] = 0.0
+    x.k_scale[int(x.block_table[2, 0])] *= -1.0
+    out, lse, _ = run(x, 4)
+    ref_o, ref_l = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    compare(out, lse, ref_o, ref_l, "fp8 negative / zero page scales", tol_o=range_tol(ref_o))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fp8_unused_slots_and_pages_are_never_read_bitwise(h_q):
+    _say(f"fp8: garbage codes in unused slots, NaN codes in unused pages, h_q={h_q}")
     seqlens = (70, 130, 3)
-    x = make_inputs(3, 1, 16, "bf16", seqlens=seqlens, seed=29, extra_pages=4, kv_dtype="fp8")
+    x = make_inputs(3, 1, h_q, "bf16", seqlens=seqlens, seed=29, extra_pages=4, kv_dtype="fp8")
     out1, lse1, _ = run(x, 4)
     raw = x.k_cache.view(torch.uint8)
     for b, nlen in enumerate(seqlens):
@@ -356,7 +388,7 @@ def _full_reference(idx, x):
 
 
 @pytest.mark.parametrize("entry", ENTRIES)
-@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 11, 12])
 def test_workload_full_size_every_request(idx, entry):
     """Full-size workload in the launch configuration the benchmark uses;
     every request is checked against the oracle (max |dO|, max |dLSE|), and
