@@ -412,6 +412,11 @@ def shader_clock_mhz():
     while decode steps are running, so it is the clock under this load."""
     import subprocess
 
+    # Under rocprofv3 every child process starts with the profiler preloaded,
+    # which initialises the GPU before rocm-smi's launcher hands over to
+    # Python: no probe there.
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     for cmd in (["rocm-smi", "--showclocks"], ["/opt/rocm/bin/rocm-smi", "--showclocks"]):
         try:
             out = subprocess.run(cmd, capture_output=True, text=True, timeout=20).stdout
@@ -442,7 +447,8 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     host = workload_inputs(idx)
     g = host.to(torch.device("cuda:0"))
     caches = [g.k_cache] + [g.k_cache.clone() for _ in range(max(1, copies) - 1)]
-    sched0, _ = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q)
+    F = api.FIXED_OVERHEAD
+    sched0, _ = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q, fixed_overhead=F)
     num_parts = sched0.shape[0]
     bufs = api.DecodeBuffers(g.q, num_parts)
     torch.cuda.synchronize()
@@ -450,7 +456,7 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     def step(i, ev=None):
         if ev is not None:
             ev[0].record()
-        meta = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q, num_parts=num_parts)
+        meta = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q, num_parts=num_parts, fixed_overhead=F)
         k = caches[i % len(caches)]
         if ev is not None:
             ev[1].record()
@@ -477,7 +483,7 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     res = {
-        "workload": w, "host": host, "num_parts": num_parts, "copies": len(caches),
+        "workload": w, "host": host, "num_parts": num_parts, "fixed_overhead": F, "copies": len(caches),
         "region_ms": max(t_start.elapsed_time(t_end), wall * 1e3),
         "meta_ms": [e[0].elapsed_time(e[1]) for e in events],
         "splitkv_ms": [e[1].elapsed_time(e[2]) for e in events],
@@ -521,7 +527,8 @@ def mla_record(idx: int, m: dict, warm: dict) -> dict:
     kv_med_s = sk["median"] * 1e-3        # seconds
     rec = {
         "config": idx, "workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "dtype": w.dtype,
-        "causal": w.causal, "s_k": w.description, "num_parts": m["num_parts"], "kv_copies": m["copies"],
+        "causal": w.causal, "s_k": w.description, "num_parts": m["num_parts"],
+        "sched_fixed_overhead": m["fixed_overhead"], "kv_copies": m["copies"],
         "bound": bound,
         "step_us": {k: round(v * 1e3, 2) for k, v in st.items()},
         "ms_per_step_region": round(ms_step, 5),
@@ -709,7 +716,8 @@ def main() -> int:
         "data": "synthetic: seeded randn q/KV, shuffled 64-token page table",
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
                    "s_k": "4096" if headline == 2 else w.description, "d_k": D_K, "d_v": D_V,
-                   "page": PAGE, "causal": w.causal, "num_parts": m["num_parts"], "kv_copies": m["copies"],
+                   "page": PAGE, "causal": w.causal, "num_parts": m["num_parts"],
+                   "sched_fixed_overhead": m["fixed_overhead"], "kv_copies": m["copies"],
                    "kv_cache": "fp8_e4m3 + per-page fp32 scale" if w.kv == "fp8" else w.dtype},
         "effective_hbm_gbps": rec["step_gbps"],
         "effective_hbm_frac": round(rec["step_gbps"] / HBM_PEAK_GBPS, 4),

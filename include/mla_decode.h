@@ -154,6 +154,18 @@ mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, in
                             int num_parts, int32_t* sched, int32_t* split_offsets, hipStream_t stream);
 
 /*
+ * mla_get_metadata with the per-piece overhead F given explicitly, 0 <= F <= 64
+ * (INVALID_VALUE otherwise), for the same quota rule of page "FlashMLA:
+ * 高性能GPU注意力机制计算库 文件结构分析", section "6. SM资源调度优化".  Every F
+ * gives a valid schedule for every decode entry point; F only moves the cuts
+ * (mla_get_metadata uses MLA_FIXED_OVERHEAD).  The cost bound becomes
+ * sum_b (P_b + F) < 2^31.
+ */
+mla_status mla_get_metadata_ex(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                               int num_parts, int fixed_overhead, int32_t* sched, int32_t* split_offsets,
+                               hipStream_t stream);
+
+/*
  * Bytes of device workspace the decode entry points need.  The pieces a split
  * request is cut into are merged by their LSE in a second kernel (page
  * "FlashMLA 在 Hopper GPU 上的 MHA 内核调度优化解析", section

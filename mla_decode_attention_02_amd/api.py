@@ -19,6 +19,7 @@ D_K = 576
 D_V = 512
 PAGE = 64
 SCHED_FIELDS = 8
+FIXED_OVERHEAD = 2               # MLA_FIXED_OVERHEAD: pages a piece's set-up and merge cost
 
 _LIB_NAME = "libmla_decode.so"
 _lib = None
@@ -109,6 +110,8 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.mla_get_metadata_shape.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
     L.mla_get_metadata.restype = st
     L.mla_get_metadata.argtypes = [p, i, i, i, i, i, p, p, p]
+    L.mla_get_metadata_ex.restype = st
+    L.mla_get_metadata_ex.argtypes = [p, i, i, i, i, i, i, p, p, p]
     L.mla_workspace_size.restype = st
     L.mla_workspace_size.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     for name in ("mla_decode", "mla_decode_splitkv", "mla_decode_combine", "mla_decode_fused",
@@ -169,9 +172,12 @@ def get_metadata_shape(batch: int, s_q: int, h_q: int, h_kv: int = 1, num_cus: i
 
 
 def get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int = 1,
-                 num_parts: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 num_parts: Optional[int] = None,
+                 fixed_overhead: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Split-KV tile schedule for one decode step: (sched [num_parts, 8],
-    split_offsets [batch + 1]), both int32 on the device of cache_seqlens."""
+    split_offsets [batch + 1]), both int32 on the device of cache_seqlens.
+    `fixed_overhead` (pages per piece, default FIXED_OVERHEAD) only moves the
+    cuts: every value gives a valid schedule."""
     if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.dim() != 1:
         raise ValueError("cache_seqlens must be a 1-D int32 device tensor")
     seq = cache_seqlens.contiguous()
@@ -181,8 +187,9 @@ def get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int = 1,
             num_parts, _, _ = get_metadata_shape(batch, s_q, h_q, h_kv)
     sched = torch.empty((num_parts, SCHED_FIELDS), dtype=torch.int32, device=seq.device)
     offs = torch.empty((batch + 1,), dtype=torch.int32, device=seq.device)
-    _check(lib().mla_get_metadata(seq.data_ptr(), batch, s_q, h_q, h_kv, num_parts,
-                                  sched.data_ptr(), offs.data_ptr(), _stream_ptr(seq.device)))
+    F = FIXED_OVERHEAD if fixed_overhead is None else int(fixed_overhead)
+    _check(lib().mla_get_metadata_ex(seq.data_ptr(), batch, s_q, h_q, h_kv, num_parts, F,
+                                     sched.data_ptr(), offs.data_ptr(), _stream_ptr(seq.device)))
     return sched, offs
 
 

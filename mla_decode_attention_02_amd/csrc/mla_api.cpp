@@ -213,13 +213,22 @@ mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
 
 mla_status mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
                             int num_parts, int32_t* sched, int32_t* split_offsets, hipStream_t stream) {
+  return mla_get_metadata_ex(cache_seqlens, batch, s_q, h_q, h_kv, num_parts, MLA_FIXED_OVERHEAD, sched,
+                             split_offsets, stream);
+}
+
+mla_status mla_get_metadata_ex(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                               int num_parts, int fixed_overhead, int32_t* sched, int32_t* split_offsets,
+                               hipStream_t stream) {
   mla_status st = check_shape(batch, s_q, h_q, h_kv);
   if (st != MLA_SUCCESS) return st;
   if (num_parts <= 0) return fail(MLA_ERROR_INVALID_VALUE, "num_parts must be positive");
+  if (fixed_overhead < 0 || fixed_overhead > 64)
+    return fail(MLA_ERROR_INVALID_VALUE, "fixed_overhead must lie in [0, 64] (got %d)", fixed_overhead);
   if (!cache_seqlens || !sched || !split_offsets) return fail(MLA_ERROR_INVALID_VALUE, "NULL pointer");
   if (!aligned(cache_seqlens, 4) || !aligned(sched, 4) || !aligned(split_offsets, 4))
     return fail(MLA_ERROR_INVALID_VALUE, "int32 arrays must be 4-byte aligned");
-  hipError_t e = mla::launch_metadata(cache_seqlens, batch, 1, num_parts, MLA_FIXED_OVERHEAD, sched,
+  hipError_t e = mla::launch_metadata(cache_seqlens, batch, 1, num_parts, fixed_overhead, sched,
                                       split_offsets, stream);
   if (e != hipSuccess) return hip_fail(e, "metadata launch");
   return ok();

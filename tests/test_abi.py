@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("mla_last_error", "mla_abi_version", "mla_get_metadata_shape", "mla_get_metadata",
+    for n in ("mla_last_error", "mla_abi_version", "mla_get_metadata_shape", "mla_get_metadata", "mla_get_metadata_ex",
               "mla_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
               "mla_decode_fused", "mla_decode_noalloc", "mla_check_paged_inputs", "mla_merge_partials",
               "mha_get_metadata_shape",
@@ -95,6 +95,17 @@ def test_get_metadata_rejects_before_launch(L):
     assert L.mla_get_metadata(fake, 2, 1, 16, 1, 0, fake, fake, None) == INVALID
     assert L.mla_get_metadata(fake, 2, 1, 16, 3, 4, fake, fake, None) == UNSUPPORTED
     assert L.mla_get_metadata(fake + 2, 2, 1, 16, 1, 4, fake, fake, None) == INVALID
+    for F in (-1, 65):
+        assert L.mla_get_metadata_ex(fake, 2, 1, 16, 1, 4, F, fake, fake, None) == INVALID
+        assert "fixed_overhead" in L.mla_last_error().decode()
+    assert L.mla_get_metadata_ex(None, 2, 1, 16, 1, 4, 4, fake, fake, None) == INVALID
+
+
+def test_header_binding_and_oracle_agree_on_the_overhead():
+    from oracle.metadata import FIXED_OVERHEAD
+    text = open(HEADER).read()
+    assert re.search(r"#define MLA_FIXED_OVERHEAD (\d+)", text).group(1) == str(api.FIXED_OVERHEAD)
+    assert api.FIXED_OVERHEAD == FIXED_OVERHEAD
 
 
 def _valid_args():

@@ -94,6 +94,22 @@ def test_metadata_bit_exact(seqlens, parts):
     assert np.array_equal(offs.cpu().numpy(), ref_o)
 
 
+@pytest.mark.parametrize("F", [0, 1, 4, 9, 64])
+@pytest.mark.parametrize("seqlens,parts", [
+    ([640, 192, 0, 65], 3),
+    ([(i * 37) % 900 for i in range(9000)], 256),
+    ([(i * 53) % 300 for i in range(20000)], 256),   # beyond the scheduler's LDS staging
+], ids=["small", "9000", "20000"])
+def test_metadata_explicit_overhead_bit_exact(seqlens, parts, F):
+    _say(f"metadata F={F} batch={len(seqlens)} parts={parts}")
+    seq = torch.tensor(seqlens, dtype=torch.int32, device="cuda:0")
+    sched, offs = api.get_metadata(seq, 1, 16, num_parts=parts, fixed_overhead=F)
+    torch.cuda.synchronize()
+    ref_s, ref_o = oracle_metadata(seqlens, parts, fixed_overhead=F)
+    assert np.array_equal(sched.cpu().numpy(), ref_s)
+    assert np.array_equal(offs.cpu().numpy(), ref_o)
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 11, 12])
 def test_metadata_workloads_bit_exact(idx):
     w = WORKLOADS[idx]
