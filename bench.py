@@ -21,8 +21,9 @@ every request).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
-Workloads 7 and 8 time the paged grouped-query (MHA) path instead: schedule
-(mha_get_metadata), split-KV kernel and combine over separate K and V caches.
+--workload N times one workload alone: 1-5 as above, 6, 11 and 12 the fp8-cache
+variants of 3, 2 and 5, and 7-10 the paged grouped-query (MHA) path (schedule
+mha_get_metadata, split-KV kernel and combine over separate K and V caches).
 """
 
 from __future__ import annotations
