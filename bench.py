@@ -575,14 +575,16 @@ def cpu_leg(m: dict, seconds: float, check_all: bool = True):
     out = m["out"].numpy().reshape(B, R, D_V)
     lse = m["lse"].numpy().reshape(B, R)
     base = None
-    ref = {}
+    ref, t_req = {}, {}
     if seconds > 0:
         done, flops = 0, 0.0
         t0 = time.perf_counter()
         while True:
             b = done % B
+            tb = time.perf_counter()
             o, l = oracle_decode_rows(qf, kf, host.block_table, host.cache_seqlens, host.softmax_scale,
                                       host.causal, b)
+            t_req.setdefault(b, time.perf_counter() - tb)
             ref.setdefault(b, (o, l))
             flops += 2.0 * R * seq[b] * (D_K + D_V)
             done += 1
@@ -595,8 +597,13 @@ def cpu_leg(m: dict, seconds: float, check_all: bool = True):
     todo = range(B) if check_all else sorted(ref)
     dO, dL, num, den = 0.0, 0.0, 0.0, 0.0
     for b in todo:
-        o, l = ref[b] if b in ref else oracle_decode_rows(qf, kf, host.block_table, host.cache_seqlens,
-                                                          host.softmax_scale, host.causal, b)
+        if b in ref:
+            o, l = ref[b]
+        else:
+            tb = time.perf_counter()
+            o, l = oracle_decode_rows(qf, kf, host.block_table, host.cache_seqlens, host.softmax_scale,
+                                      host.causal, b)
+            t_req[b] = time.perf_counter() - tb
         fin = np.isfinite(l)
         d = out[b] - o
         dO = max(dO, float(np.abs(d).max()))
@@ -608,6 +615,10 @@ def cpu_leg(m: dict, seconds: float, check_all: bool = True):
               "rms_rel_dO": (num / den) ** 0.5 if den > 0 else 0.0,
               "tolerance": {"max_abs_dO": 1.5e-2, "max_abs_dLSE": 1e-3, "rms_rel_dO": 1e-2}}
     parity["within_tolerance"] = bool(dO <= 1.5e-2 and dL <= 1e-3 and parity["rms_rel_dO"] <= 1e-2)
+    if len(t_req) == B:
+        # the oracle's wall time over the whole workload (each request once)
+        parity["oracle_seconds_whole_workload"] = round(sum(t_req.values()), 3)
+        parity["oracle_cores"] = int(threads)
     return base, parity
 
 
