@@ -651,8 +651,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=None,
-                    help="one workload only, 1..10 (default: the five configurations 1-5, headline 2); 6 is 3 "
-                         "with an fp8 cache, 7-10 use the MHA path (7-9 GQA, 9 with fp8 K/V; 10 multi-query)")
+                    help="one workload only, 1..12 (default: the five configurations 1-5, headline 2); 6, 11 "
+                         "and 12 are 3, 2 and 5 with an fp8 cache, 7-10 use the MHA path (7-9 GQA, 9 with fp8 "
+                         "K/V; 10 multi-query)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
