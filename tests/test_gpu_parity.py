@@ -358,6 +358,21 @@ def test_split_counts_agree(h_q):
     assert np.abs(l1 - l2).max() <= 1e-4
 
 
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("h_q,seqlens,parts", [
+    (16, (12800, 70), 150),        # ~100 pieces: the combine reduces its LSEs in groups of 64
+    (128, (25600, 1, 640), 256),   # ~200 pieces: four groups, the last partial
+], ids=["hq16_100pieces", "hq128_200pieces"])
+def test_requests_cut_into_more_than_64_pieces(h_q, seqlens, parts, entry):
+    _say(f"many pieces {entry} h_q={h_q} seqlens={seqlens} parts={parts}")
+    x = make_inputs(len(seqlens), 1, h_q, "bf16", seqlens=seqlens, seed=61 + h_q, poison=True)
+    out, lse, meta = run(x, parts, entry)
+    pieces = np.diff(meta[1])
+    assert pieces.max() > 64, f"expected a request cut into more than 64 pieces, got {pieces.max()}"
+    ref_o, ref_l = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    compare(out, lse, ref_o, ref_l, f"many pieces h_q={h_q}")
+
+
 # ------------------------------------------------------------ fused path --
 @pytest.mark.parametrize("h_q", [16, 128])
 def test_fused_repeated_calls_reuse_counters(h_q):
