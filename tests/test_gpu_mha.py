@@ -111,6 +111,22 @@ def test_mha_small_parity(s_q, h_q, h_kv, d, seqlens, causal, dtype, parts):
     compare(out, lse, ref_o, ref_l, tag)
 
 
+@pytest.mark.parametrize("h_q,h_kv,d,seqlens,parts,kv", [
+    (8, 1, 128, (12800, 70), 150, "same"),      # ~100 pieces of one unit
+    (16, 2, 64, (25600, 1), 300, "same"),       # two units of ~130 pieces each
+    (8, 1, 128, (12800,), 150, "fp8"),          # the key-split kernel's pieces
+], ids=["d128_100pieces", "d64_2units_130pieces", "fp8_100pieces"])
+def test_mha_units_cut_into_more_than_64_pieces(h_q, h_kv, d, seqlens, parts, kv):
+    _say(f"mha many pieces h_q={h_q} h_kv={h_kv} d={d} seqlens={seqlens} parts={parts} {kv}")
+    x = make_mha_inputs(len(seqlens), 1, h_q, h_kv, d, "bf16", seqlens=seqlens, seed=71 + d, poison=True,
+                        kv_dtype=kv)
+    out, lse, meta = run(x, parts)
+    assert np.diff(meta[1]).max() > 64, "expected a unit cut into more than 64 pieces"
+    kf, vf = kv64(x)
+    ref_o, ref_l = oracle_mha_decode(x.q, kf, vf, x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    compare(out, lse, ref_o, ref_l, f"mha many pieces {kv}")
+
+
 def test_mha_empty_requests_and_masked_rows():
     _say("mha empty request / fully masked causal rows")
     x = make_mha_inputs(3, 3, 8, 2, 128, "bf16", seqlens=(0, 1, 70), causal=True, seed=5, poison=True)
