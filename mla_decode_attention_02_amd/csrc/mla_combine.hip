@@ -8,8 +8,9 @@
 // The lanes load the pieces' LSEs together (lane k holds piece k of a group of
 // 64) and reduce them across the wave, while the first eight pieces' data loads
 // are already in flight; the weighted sum keeps eight pieces' loads in flight
-// per lane, so a request cut into many pieces is not a chain of dependent
-// memory round trips.  Requests with no cached token get
+// per lane (sixteen with half rows: the next eight are issued before the
+// current eight are summed), so a request cut into many pieces is not a chain
+// of dependent memory round trips.  Requests with no cached token get
 // O = 0 and LSE = -inf; whole (unsplit) requests, and split requests the
 // split-KV kernel merged itself (at most fuse_max pieces), are skipped.
 #include "mla_common.hpp"
@@ -65,9 +66,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     }
   };
   if (ns <= 64) {
-    // the first eight pieces' data loads go out together with the LSE loads
-    f32x4 v[8][kCh];
-    load8(v, 0, ns);
+    // the first eight pieces' data loads go out together with the LSE loads;
+    // with half rows per wave (few rows, so typically many pieces each) the
+    // next eight pieces' loads are issued before the current eight are summed
+    f32x4 v[kCh == 1 ? 2 : 1][8][kCh];
+    load8(v[0], 0, ns);
     const float lk = lane < ns ? lse_k[(int64_t)lane * p.rows] : -INFINITY;
     const float mx = wave_max(lk);
     if (mx != -INFINITY) {
@@ -75,10 +78,19 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
       const float sum = wave_sum(e);
       L = mx + __logf(sum);
       const float w = e / sum;                                      // exp(LSE_k - LSE)
-      acc8(v, w, 0);
-      for (int j = 8; j < ns; j += 8) {
-        load8(v, j, ns);
-        acc8(v, w, j);
+      if constexpr (kCh == 1) {
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi) {
+          if (gi * 8 >= ns) break;
+          if (gi * 8 + 8 < ns) load8(v[(gi + 1) & 1], gi * 8 + 8, ns);
+          acc8(v[gi & 1], w, gi * 8);
+        }
+      } else {
+        acc8(v[0], w, 0);
+        for (int j = 8; j < ns; j += 8) {
+          load8(v[0], j, ns);
+          acc8(v[0], w, j);
+        }
       }
     }
   } else {
