@@ -1,8 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of paged MLA decode on one MI355X.
 
-One step = the whole decode path over one batch: the tile schedule
-(mla_get_metadata), the split-KV attention kernel and the combine kernel.  By
+One step = the whole decode path over one batch: the tile schedule, the
+split-KV attention kernel and the combine kernel.  The schedule is derived
+inside both kernels (each workgroup evaluates the scheduler's rule from
+cache_seqlens), so a step is two launches; the three-launch form with the
+schedule precomputed by mla_get_metadata is timed after it and reported
+beside it (metadata_us_median, step_us_median_precomputed_schedule).  By
 default the five configurations are measured one after the other (1 tiny, 2
 B64 h_q128 s_k4096 -- the headline --, 3 variable-length h_q16, 4 two-token
 causal fp16, 5 four long requests), inputs seeded and synthetic, 64-token pages
@@ -48,10 +52,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mla_decode_attention_02_amd", "csrc")
 # sources whose change invalidates stored hardware counters of a kernel
 KERNEL_SOURCES = {
-    "splitkv_wide_kernel": ["mla_splitkv_wide.hip", "mla_splitkv.hpp", "mla_common.hpp"],
-    "splitkv_narrow_kernel": ["mla_splitkv_narrow.hip", "mla_splitkv.hpp", "mla_common.hpp"],
-    "splitkv_fp8_kernel": ["mla_splitkv_fp8.hip", "mla_fp8.hpp", "mla_splitkv.hpp", "mla_common.hpp"],
-    "splitkv_wide_fp8_kernel": ["mla_splitkv_wide8.hip", "mla_fp8.hpp", "mla_splitkv.hpp", "mla_common.hpp"],
+    "splitkv_wide_kernel": ["mla_splitkv_wide.hip", "mla_splitkv.hpp", "mla_sched.hpp", "mla_common.hpp"],
+    "splitkv_narrow_kernel": ["mla_splitkv_narrow.hip", "mla_splitkv.hpp", "mla_sched.hpp", "mla_common.hpp"],
+    "splitkv_fp8_kernel": ["mla_splitkv_fp8.hip", "mla_fp8.hpp", "mla_splitkv.hpp", "mla_sched.hpp", "mla_common.hpp"],
+    "splitkv_wide_fp8_kernel": ["mla_splitkv_wide8.hip", "mla_fp8.hpp", "mla_splitkv.hpp", "mla_sched.hpp", "mla_common.hpp"],
     "mha_splitkv_kernel": ["mha_decode.hip", "mla_common.hpp"],
     "mha_keysplit_kernel": ["mha_decode.hip", "mla_common.hpp"],
 }
@@ -183,6 +187,7 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
     w = MHA_WORKLOADS[workload] if mha else WORKLOADS[workload]
     kernel = mha_kernel_name(w) if mha else mla_kernel_name(w)
     tag = f"w{workload}"
+    ref = "" if mha else " --no-reference"       # only the timed form's launches in the trace
     stats = _counter_rows(os.path.join(out_dir, f"prof_{tag}", f"{tag}_kernel_stats.csv"))
 
     def per_dispatch(sub, counter, name_part):
@@ -223,19 +228,19 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
              "Commands (from the repository root on one MI355X, TMPDIR=/tmp):", "",
              "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{tag} -o {tag} -- "
-             f"python3 bench.py --workload {workload} --steps 20 --warmup 5 --no-cpu-baseline",
+             f"python3 bench.py --workload {workload} --steps 20 --warmup 5 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_{tag} -o p -- "
-             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline",
+             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_{tag} -o p -- "
-             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline",
+             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_copy -o p -- "
              f"python3 bench.py --calibrate-copy {COPY_MIB}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_copy -o p -- "
              f"python3 bench.py --calibrate-copy {COPY_MIB}",
              f"rocprofv3 --pmc {' '.join(MFMA_PASS)} --output-format csv -d gpurun_out/pmcm_{tag} -o p -- "
-             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline",
+             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc {' '.join(LDS_PASS)} --output-format csv -d gpurun_out/pmcl_{tag} -o p -- "
-             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline",
+             f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
              f"python3 bench.py --summarize-profiles gpurun_out --workload {workload}",
              "```", "", "Kernel trace statistics (--stats):", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -324,30 +329,30 @@ def bench_mha(args) -> dict:
         meta = api.mha_get_metadata(g.cache_seqlens, w.s_q, w.h_q, w.h_kv, num_parts=num_parts)
         k, v = caches[i % len(caches)]
         if ev is not None:
-            ev[0].record()
+            ev[0].record(ev[1])
         api.mha_decode_splitkv(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
                                g.k_scale, g.v_scale)
         if ev is not None:
-            ev[1].record()
+            ev[0].record(ev[1] + 1)
         api.mha_decode_combine(g.q, k, v, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
                                g.k_scale, g.v_scale)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    ev = HipEvents(2 * args.steps)               # around the split-KV kernel of every step
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(args.warmup + i, (ev, 2 * i))
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = max(t0.elapsed_time(t1), wall * 1e3) / args.steps
-    ks = sorted(a.elapsed_time(b) for a, b in events)
+    ks = sorted(ev.ms(2 * i, 2 * i + 1) for i in range(args.steps))
+    ev.close()
     kavg = sum(ks) / len(ks)
     ach = splitkv_bytes / (kavg * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -401,6 +406,72 @@ def bench_mha(args) -> dict:
     return result
 
 
+class HipEvents:
+    """A pool of HIP timing events recorded on torch's current stream, created
+    with hipEventDisableSystemFence: recording one then skips the system-scope
+    memory fence, which the default events (torch.cuda.Event) pay on every
+    record (≈ 4.5 µs of a step each on MI355X, against ≈ 1.5 µs).  The
+    timestamps are the same; the host only reads them after a synchronize."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+
+        import torch
+
+        self._c = ctypes
+        self._hip = self._runtime()
+        self._stream = torch.cuda.current_stream().cuda_stream
+        self._ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self._ev.append(e)
+
+    @staticmethod
+    def _runtime():
+        """The HIP runtime this process already runs on (the one torch and
+        libmla_decode.so share), not a second copy."""
+        import ctypes
+
+        path = "libamdhip64.so"
+        try:
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+        except OSError:
+            pass
+        L = ctypes.CDLL(path)
+        L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        return L
+
+    def record(self, i: int) -> None:
+        if self._hip.hipEventRecord(self._ev[i], self._stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i: int, j: int) -> float:
+        t = self._c.c_float()
+        if self._hip.hipEventElapsedTime(self._c.byref(t), self._ev[i], self._ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self) -> None:
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
+
+
+def _median_us(xs):
+    return None if not xs else round(_quantiles(xs)["median"] * 1e3, 2)
+
+
 def _quantiles(xs):
     """Median, p10 and p90 of a list of times (any unit), as a dict."""
     v = sorted(xs)
@@ -429,14 +500,18 @@ def shader_clock_mhz():
     return None
 
 
-def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: bool = False) -> dict:
-    """Time one MLA workload on cuda:0.  One step = mla_get_metadata + split-KV
-    + combine over the whole batch, inputs resident in HBM; steps rotate over
-    `copies` independent KV caches (copies >= 2 and a cache larger than the
-    last-level caches: every step reads its pages from HBM).  Each phase is
-    bracketed by HIP events on the stream the library launches on (torch's
-    current stream).  Returns per-step lists (ms) and the outputs of the
-    last step."""
+def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: bool = False,
+                reference: bool = True) -> dict:
+    """Time one MLA workload on cuda:0.  One step = split-KV + combine over the
+    whole batch with the schedule derived inside both kernels (no schedule
+    passed: each workgroup evaluates the scheduler's rule from cache_seqlens),
+    inputs resident in HBM; steps rotate over `copies` independent KV caches
+    (copies >= 2 and a cache larger than the last-level caches: every step
+    reads its pages from HBM).  The same steps with the schedule precomputed
+    by mla_get_metadata (three launches) are timed after them for reference.
+    Each phase is bracketed by HIP events on the stream the library launches
+    on (torch's current stream).  Returns per-step lists (ms) and the outputs
+    of the last step."""
     import threading
 
     import torch
@@ -454,44 +529,65 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     bufs = api.DecodeBuffers(g.q, num_parts)
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def step(i, ev=None, precomputed=False):
+        """One step; with `ev` = (events, base) it records events base + 0
+        (start), + 1 (after the schedule, precomputed form only) and + 2
+        (after the split-KV kernel)."""
         if ev is not None:
-            ev[0].record()
-        meta = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q, num_parts=num_parts, fixed_overhead=F)
+            ev[0].record(ev[1])
+        if precomputed:
+            meta = api.get_metadata(g.cache_seqlens, w.s_q, w.h_q, num_parts=num_parts, fixed_overhead=F)
+            if ev is not None:
+                ev[0].record(ev[1] + 1)
+        else:
+            meta = num_parts                       # the kernels derive the schedule themselves
         k = caches[i % len(caches)]
-        if ev is not None:
-            ev[1].record()
         api.mla_decode_splitkv(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
                                g.k_scale)
         if ev is not None:
-            ev[2].record()
+            ev[0].record(ev[1] + 2)
         api.mla_decode_combine(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
                                g.k_scale)
-        if ev is not None:
-            ev[3].record()
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # timed region: two events per step (start, after split-KV); a step ends
+    # where the next one starts, the last one at an end event
+    ev = HipEvents(3 * steps + 1)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        step(warmup + i, events[i])
+        step(warmup + i, (ev, 3 * i))
+    ev.record(3 * steps)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    nxt = [3 * (i + 1) for i in range(steps)]
     res = {
         "workload": w, "host": host, "num_parts": num_parts, "fixed_overhead": F, "copies": len(caches),
         "region_ms": max(t_start.elapsed_time(t_end), wall * 1e3),
-        "meta_ms": [e[0].elapsed_time(e[1]) for e in events],
-        "splitkv_ms": [e[1].elapsed_time(e[2]) for e in events],
-        "combine_ms": [e[2].elapsed_time(e[3]) for e in events],
-        "step_ms": [e[0].elapsed_time(e[3]) for e in events],
+        "splitkv_ms": [ev.ms(3 * i, 3 * i + 2) for i in range(steps)],
+        "combine_ms": [ev.ms(3 * i + 2, nxt[i]) for i in range(steps)],
+        "step_ms": [ev.ms(3 * i, nxt[i]) for i in range(steps)],
         "out": bufs.out.float().cpu(), "lse": bufs.lse.cpu(),
     }
+    ev.close()
+    # reference: the same steps with the schedule precomputed by mla_get_metadata
+    res["meta_ms"] = res["pre_step_ms"] = res["pre_splitkv_ms"] = None
+    n_pre = max(1, min(steps, 50)) if reference else 0
+    if n_pre:
+        ev = HipEvents(3 * n_pre + 1)
+        for i in range(n_pre):
+            step(warmup + steps + i, (ev, 3 * i), precomputed=True)
+        ev.record(3 * n_pre)
+        torch.cuda.synchronize()
+        res["meta_ms"] = [ev.ms(3 * i, 3 * i + 1) for i in range(n_pre)]
+        res["pre_step_ms"] = [ev.ms(3 * i, 3 * i + 3) for i in range(n_pre)]
+        res["pre_splitkv_ms"] = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(n_pre)]
+        ev.close()
     if clock_probe:
         # sample the shader clock while the same steps keep the GPU busy
         got = {}
@@ -535,7 +631,10 @@ def mla_record(idx: int, m: dict, warm: dict) -> dict:
         "ms_per_step_region": round(ms_step, 5),
         "splitkv_us": {k: round(v * 1e3, 2) for k, v in sk.items()},
         "combine_us_median": round(_quantiles(m["combine_ms"])["median"] * 1e3, 2),
-        "metadata_us_median": round(_quantiles(m["meta_ms"])["median"] * 1e3, 2),
+        "schedule": "derived in the split-KV and combine kernels (no metadata launch)",
+        "metadata_us_median": _median_us(m["meta_ms"]),
+        "step_us_median_precomputed_schedule": _median_us(m["pre_step_ms"]),
+        "splitkv_us_median_precomputed_schedule": _median_us(m["pre_splitkv_ms"]),
         "warm_step_us_median": round(_quantiles(warm["step_ms"])["median"] * 1e3, 2),
         "warm_note": "one KV cache reused every step (its pages may stay in L2/MALL)",
         "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -655,6 +754,9 @@ def main() -> int:
                          "and 12 are 3, 2 and 5 with an fp8 cache, 7-10 use the MHA path (7-9 GQA, 9 with fp8 "
                          "K/V; 10 multi-query)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the reference steps with a precomputed schedule (profiled runs: only the "
+                         "timed form's launches in the trace)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU leg (oracle timing and the parity check against it)")
@@ -699,8 +801,9 @@ def main() -> int:
         print(f"bench: workload {idx}", file=sys.stderr, flush=True)
         # warm (one cache) first: the clock probe that follows the timed steps
         # keeps the GPU busy for seconds and would heat the part for it
-        warm = measure_mla(idx, max(20, args.steps // 4), args.warmup, 1)
-        m = measure_mla(idx, args.steps, args.warmup, args.copies, clock_probe=(idx == headline))
+        warm = measure_mla(idx, max(20, args.steps // 4), args.warmup, 1, reference=False)
+        m = measure_mla(idx, args.steps, args.warmup, args.copies, clock_probe=(idx == headline),
+                        reference=not args.no_reference)
         rec = mla_record(idx, m, warm)
         if idx == headline:
             rec["sclk_mhz_observed"] = m.get("sclk_mhz")
@@ -740,8 +843,10 @@ def main() -> int:
         "roofline": headline_roofline(rec),
         "step_us": rec["step_us"],
         "warm_step_us_median": rec["warm_step_us_median"],
-        "metadata_us_median": rec["metadata_us_median"],
         "combine_us_median": rec["combine_us_median"],
+        "schedule": rec["schedule"],
+        "metadata_us_median": rec["metadata_us_median"],
+        "step_us_median_precomputed_schedule": rec["step_us_median_precomputed_schedule"],
     }
     if base is not None:
         result["cpu_baseline"] = base

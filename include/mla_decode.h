@@ -42,8 +42,9 @@
  *    block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages)
  *    (these two are checked on the device by mla_check_paged_inputs, and by
  *    every decode entry point when the environment variable MLA_DEBUG is set);
- *    `sched` / `split_offsets` were produced by mla_get_metadata from the same
- *    cache_seqlens with the same num_parts; cache contents are finite; the total
+ *    `sched` / `split_offsets`, when given, were produced by mla_get_metadata
+ *    from the same cache_seqlens with the same num_parts; cache contents are
+ *    finite; the total
  *    schedule cost sum_b (ceil(cache_seqlens[b] / 64) + MLA_FIXED_OVERHEAD) is
  *    below 2^31.
  *  - Thread safety: all entry points may be called concurrently; the error
@@ -195,9 +196,13 @@ typedef struct {
   const int32_t* block_table;  /* device [batch, max_pages_per_seq]           */
   int64_t bt_stride;           /*   stride between rows                       */
   const int32_t* cache_seqlens;/* device [batch]                              */
-  const int32_t* sched;        /* device, from mla_get_metadata               */
-  const int32_t* split_offsets;/* device, from mla_get_metadata               */
+  const int32_t* sched;        /* device, from mla_get_metadata, or NULL      */
+  const int32_t* split_offsets;/* device, from mla_get_metadata, or NULL      */
   int num_parts;               /* the num_parts the schedule was built with   */
+                               /* (both NULL: the kernels derive the schedule
+                                  of mla_get_metadata, with MLA_FIXED_OVERHEAD
+                                  and this num_parts, from cache_seqlens in
+                                  place; no metadata launch, same results)  */
   float softmax_scale;         /* finite, > 0 (typically 1/sqrt(576))         */
   int causal;                  /* 0/1; bottom-right aligned when s_q > 1      */
   void* workspace;             /* device, >= mla_workspace_size bytes, 256-B aligned */
@@ -223,9 +228,15 @@ typedef struct {
  * Alignment: q, k_cache, out must be 16-byte aligned, as must every stride
  * times the element size (q_stride[*], k_stride[0..1], out_stride[*] multiples
  * of 8); lse and the int32 arrays 4-byte aligned.
- * Errors: INVALID_VALUE (null pointer, non-positive size, bad stride or
- * alignment, non-finite or non-positive scale), UNSUPPORTED (dims, page size,
- * h_kv, dtype), WORKSPACE_TOO_SMALL, HIP (launch failed).
+ * Schedule: with sched and split_offsets NULL, every workgroup of the two
+ * kernels evaluates the scheduler's rule (see mla_get_metadata) for its own
+ * partition or request from cache_seqlens, so a decode step needs no
+ * mla_get_metadata call; a caller that reuses one schedule across many
+ * layers may still pass it precomputed.
+ * Errors: INVALID_VALUE (null pointer, exactly one of sched / split_offsets
+ * NULL, non-positive size, bad stride or alignment, non-finite or
+ * non-positive scale), UNSUPPORTED (dims, page size, h_kv, dtype),
+ * WORKSPACE_TOO_SMALL, HIP (launch failed).
  */
 mla_status mla_decode(const mla_decode_args* args, hipStream_t stream);
 

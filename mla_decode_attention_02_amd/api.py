@@ -220,7 +220,7 @@ def workspace_size(batch: int, s_q: int, h_q: int, num_parts: int) -> int:
 
 
 def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
-                workspace, out, lse, k_scale=None) -> DecodeArgs:
+                workspace, out, lse, k_scale=None, num_parts=None) -> DecodeArgs:
     a = DecodeArgs()
     a.dtype = DTYPE_CODES[q.dtype]
     a.batch, a.s_q, a.h_q = q.shape[0], q.shape[1], q.shape[2]
@@ -235,9 +235,9 @@ def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, s
     a.block_table = block_table.data_ptr()
     a.bt_stride = block_table.stride(0)
     a.cache_seqlens = cache_seqlens.data_ptr()
-    a.sched = sched.data_ptr()
-    a.split_offsets = offs.data_ptr()
-    a.num_parts = sched.shape[0]
+    a.sched = sched.data_ptr() if sched is not None else None
+    a.split_offsets = offs.data_ptr() if offs is not None else None
+    a.num_parts = sched.shape[0] if sched is not None else num_parts
     a.softmax_scale = float(softmax_scale)
     a.causal = 1 if causal else 0
     a.workspace = workspace.data_ptr() if workspace is not None else None
@@ -313,18 +313,34 @@ class DecodeBuffers:
         self.workspace = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
 
 
+def _schedule(metadata, q, k_cache):
+    """(sched, split_offsets, num_parts) of a call: get_metadata's pair, or
+    (None, None, num_parts) for the schedule the kernels derive in place from
+    cache_seqlens (metadata None: the default partition count; an int: that
+    many partitions)."""
+    if metadata is None or isinstance(metadata, int):
+        if metadata is None:
+            with torch.cuda.device(q.device):
+                parts = get_metadata_shape(q.shape[0], q.shape[1], q.shape[2], k_cache.shape[2])[0]
+        else:
+            parts = int(metadata)
+            if parts <= 0:
+                raise ValueError("the number of partitions must be positive")
+        return None, None, parts
+    sched, offs = metadata
+    _check_metadata(sched, offs, q.shape[0], q.device)
+    return sched, offs, sched.shape[0]
+
+
 def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
           k_scale=None):
     _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale)
-    if metadata is None:
-        metadata = get_metadata(cache_seqlens, q.shape[1], q.shape[2], k_cache.shape[2])
-    sched, offs = metadata
-    _check_metadata(sched, offs, q.shape[0], q.device)
+    sched, offs, parts = _schedule(metadata, q, k_cache)
     if buffers is None:
-        buffers = DecodeBuffers(q, sched.shape[0])
+        buffers = DecodeBuffers(q, parts)
     _check_outputs(q, buffers.out, buffers.lse, D_V)
     a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
-                    buffers.workspace, buffers.out, buffers.lse, k_scale)
+                    buffers.workspace, buffers.out, buffers.lse, k_scale, num_parts=parts)
     _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
     return buffers.out, buffers.lse
 
@@ -335,8 +351,10 @@ def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor
                buffers: Optional[DecodeBuffers] = None,
                k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MLA decode.  Returns (out [B, s_q, h_q, 512] in q's dtype,
-    lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result
-    (computed here when omitted); `buffers` lets a caller reuse outputs.  An
+    lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result,
+    or None (the default) / a partition count: the kernels then derive the
+    same schedule from cache_seqlens themselves, with no metadata launch;
+    `buffers` lets a caller reuse outputs.  An
     fp8 cache (torch.float8_e4m3fn, with a bf16 q) takes an
     optional per-page fp32 scale `k_scale` [num_pages] (any finite value; the
     cached row is code * scale)."""
@@ -381,10 +399,7 @@ def mla_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, block_table: torc
     to keep this function from allocating them).  Calls that overlap in time
     on one GPU share that workspace and race."""
     _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale)
-    if metadata is None:
-        metadata = get_metadata(cache_seqlens, q.shape[1], q.shape[2], k_cache.shape[2])
-    sched, offs = metadata
-    _check_metadata(sched, offs, q.shape[0], q.device)
+    sched, offs, parts = _schedule(metadata, q, k_cache)
     B, s_q, h_q, _ = q.shape
     if out is None:
         out = torch.empty((B, s_q, h_q, D_V), dtype=q.dtype, device=q.device)
@@ -392,7 +407,7 @@ def mla_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, block_table: torc
         lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
     _check_outputs(q, out, lse, D_V)
     a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs, None, out, lse,
-                    k_scale)
+                    k_scale, num_parts=parts)
     _check(lib().mla_decode_noalloc(ctypes.byref(a), _stream_ptr(q.device)))
     return out, lse
 

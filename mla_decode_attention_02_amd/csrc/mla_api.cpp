@@ -112,9 +112,10 @@ mla_status check_decode(const mla_decode_args* a) {
   if (a->k_scale && !aligned(a->k_scale, 4)) return fail(MLA_ERROR_INVALID_VALUE, "k_scale must be 4-byte aligned");
   if (a->num_pages <= 0 || a->max_pages_per_seq <= 0 || a->num_parts <= 0)
     return fail(MLA_ERROR_INVALID_VALUE, "num_pages, max_pages_per_seq and num_parts must be positive");
-  if (!a->q || !a->k_cache || !a->block_table || !a->cache_seqlens || !a->sched || !a->split_offsets ||
-      !a->workspace || !a->out || !a->lse)
+  if (!a->q || !a->k_cache || !a->block_table || !a->cache_seqlens || !a->workspace || !a->out || !a->lse)
     return fail(MLA_ERROR_INVALID_VALUE, "a required pointer is NULL");
+  if (!a->sched != !a->split_offsets)
+    return fail(MLA_ERROR_INVALID_VALUE, "sched and split_offsets must both be given or both be NULL");
   if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->workspace, 16))
     return fail(MLA_ERROR_INVALID_VALUE, "q, out and workspace must be 16-byte aligned");
   if (!aligned(a->k_cache, a->kv_dtype == MLA_KV_FP8_E4M3 ? 8 : 16))
@@ -162,6 +163,7 @@ mla::DecodeParams make_params(const mla_decode_args* a) {
   p.seqlens = a->cache_seqlens;
   p.sched = a->sched;
   p.split_offsets = a->split_offsets;
+  p.sched_f = MLA_FIXED_OVERHEAD;
   p.batch = a->batch; p.s_q = a->s_q; p.h_q = a->h_q;
   p.rows = a->s_q * a->h_q;
   p.num_parts = a->num_parts;

@@ -14,6 +14,7 @@
 // O = 0 and LSE = -inf; whole (unsplit) requests, and split requests the
 // split-KV kernel merged itself (at most fuse_max pieces), are skipped.
 #include "mla_common.hpp"
+#include "mla_sched.hpp"
 #include "mla_internal.h"
 
 namespace mla {
@@ -39,8 +40,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
   const int row = blockIdx.y * 4 + wave;
   const int col = blockIdx.z * 256 + lane * 4;
   if (row >= p.rows) return;
-  const int s0 = ldu(p.split_offsets + b);
-  const int ns = ldu(p.split_offsets + b + 1) - s0;
+  int s0, ns;
+  if (p.split_offsets) {
+    s0 = ldu(p.split_offsets + b);
+    ns = ldu(p.split_offsets + b + 1) - s0;
+  } else {
+    int before, own;
+    sched_slots(p.seqlens, p.batch, 1, p.num_parts, p.sched_f, b, before, own);
+    s0 = __builtin_amdgcn_readfirstlane(before);                    // lane 0 holds request b
+    ns = __builtin_amdgcn_readfirstlane(own);
+  }
   if (ns == 1 || (ns > 1 && ns <= p.fuse_max)) return;   // whole, or merged by the split-KV kernel
   const float* lse_k = p.part_lse + (int64_t)s0 * p.rows + row;   // stride p.rows per piece
 

@@ -150,6 +150,8 @@ BREAKS = [
     ("q null", lambda a: setattr(a, "q", None), INVALID),
     ("lse null", lambda a: setattr(a, "lse", None), INVALID),
     ("workspace null", lambda a: setattr(a, "workspace", None), INVALID),
+    ("sched null alone", lambda a: setattr(a, "sched", None), INVALID),
+    ("split_offsets null alone", lambda a: setattr(a, "split_offsets", None), INVALID),
     ("q misaligned", lambda a: setattr(a, "q", (1 << 20) + 8), INVALID),
     ("k misaligned", lambda a: setattr(a, "k_cache", (1 << 21) + 4), INVALID),
     ("lse misaligned", lambda a: setattr(a, "lse", 9 * (1 << 20) + 2), INVALID),
