@@ -32,9 +32,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // kCh = 16-byte column chunks per lane and piece: 1 (a wave covers half of
-// the 512 columns) or 2 (the whole row, chunks 256 floats apart).
+// the 512 columns) or 2 (the whole row, chunks 256 floats apart).  Pieces are
+// loaded kB at a time: 8 with half rows (few rows, so few waves, each with
+// many pieces to hide), 4 with whole rows, which keeps a wave within 64
+// registers so that eight waves share a SIMD and a launch of many rows runs
+// in one round.
 template <typename T, int kCh>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+  constexpr int kB = kCh == 1 ? 8 : 4;
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + wave;
@@ -59,16 +64,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
 #pragma unroll
   for (int h = 0; h < kCh; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = -INFINITY;
-  auto load8 = [&](f32x4 (&v)[8][kCh], int k0, int n) __attribute__((always_inline)) {
+  auto load_batch = [&](f32x4 (&v)[kB][kCh], int k0, int n) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kB; ++u)
 #pragma unroll
       for (int h = 0; h < kCh; ++h)
         v[u][h] = k0 + u < n ? *(const f32x4*)(src + (k0 + u) * piece + h * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  auto acc8 = [&](const f32x4 (&v)[8][kCh], float w, int j0) __attribute__((always_inline)) {
+  auto acc_batch = [&](const f32x4 (&v)[kB][kCh], float w, int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kB; ++u) {
       const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j0 + u));
 #pragma unroll
       for (int h = 0; h < kCh; ++h) acc[h] += wu * v[u][h];
@@ -78,8 +83,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     // the first eight pieces' data loads go out together with the LSE loads;
     // with half rows per wave (few rows, so typically many pieces each) the
     // next eight pieces' loads are issued before the current eight are summed
-    f32x4 v[kCh == 1 ? 2 : 1][8][kCh];
-    load8(v[0], 0, ns);
+    f32x4 v[kCh == 1 ? 2 : 1][kB][kCh];
+    load_batch(v[0], 0, ns);
     const float lk = lane < ns ? lse_k[(int64_t)lane * p.rows] : -INFINITY;
     const float mx = wave_max(lk);
     if (mx != -INFINITY) {
@@ -90,15 +95,15 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
       if constexpr (kCh == 1) {
 #pragma unroll
         for (int gi = 0; gi < 8; ++gi) {
-          if (gi * 8 >= ns) break;
-          if (gi * 8 + 8 < ns) load8(v[(gi + 1) & 1], gi * 8 + 8, ns);
-          acc8(v[gi & 1], w, gi * 8);
+          if (gi * kB >= ns) break;
+          if (gi * kB + kB < ns) load_batch(v[(gi + 1) & 1], gi * kB + kB, ns);
+          acc_batch(v[gi & 1], w, gi * kB);
         }
       } else {
-        acc8(v[0], w, 0);
-        for (int j = 8; j < ns; j += 8) {
-          load8(v[0], j, ns);
-          acc8(v[0], w, j);
+        acc_batch(v[0], w, 0);
+        for (int j = kB; j < ns; j += kB) {
+          load_batch(v[0], j, ns);
+          acc_batch(v[0], w, j);
         }
       }
     }
@@ -116,14 +121,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
         const int kl = k0 + lane;
         const float w = kl < ns ? __builtin_amdgcn_exp2f((lse_k[(int64_t)kl * p.rows] - L) * kLog2e) : 0.f;
         const int n = min(64, ns - k0);
-        for (int j = 0; j < n; j += 8) {
-          f32x4 v[8][kCh];
+        for (int j = 0; j < n; j += kB) {
+          f32x4 v[kB][kCh];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
+          for (int u = 0; u < kB; ++u)
 #pragma unroll
             for (int h = 0; h < kCh; ++h)
               v[u][h] = j + u < n ? *(const f32x4*)(src + (k0 + j + u) * piece + h * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
-          acc8(v, w, j);
+          acc_batch(v, w, j);
         }
       }
     }
