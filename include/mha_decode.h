@@ -37,8 +37,8 @@
  * block_table[b, 0 : ceil(cache_seqlens[b] / 64)] lie in [0, num_pages)
  * (both checked on the device by mla_check_paged_inputs, and by
  * mha_decode_splitkv / mha_decode when MLA_DEBUG is set);
- * `sched` / `split_offsets` come from mha_get_metadata with the same
- * cache_seqlens, h_kv and num_parts; the schedule cost
+ * `sched` / `split_offsets`, when given, come from mha_get_metadata with the
+ * same cache_seqlens, h_kv and num_parts; the schedule cost
  * h_kv * sum_b (ceil(cache_seqlens[b] / 64) + MLA_FIXED_OVERHEAD) is below 2^31.
  */
 #ifndef MHA_DECODE_H
@@ -103,9 +103,12 @@ typedef struct {
   const int32_t* block_table;  /* device [batch, max_pages_per_seq]           */
   int64_t bt_stride;           /*   stride between rows                       */
   const int32_t* cache_seqlens;/* device [batch]                              */
-  const int32_t* sched;        /* device, from mha_get_metadata               */
-  const int32_t* split_offsets;/* device, from mha_get_metadata               */
+  const int32_t* sched;        /* device, from mha_get_metadata, or NULL      */
+  const int32_t* split_offsets;/* device, from mha_get_metadata, or NULL      */
   int num_parts;               /* the num_parts the schedule was built with   */
+                               /* (both NULL: the kernels derive the schedule
+                                  of mha_get_metadata for this num_parts from
+                                  cache_seqlens in place, as mla_decode does) */
   float softmax_scale;         /* finite, > 0 (typically 1/sqrt(head_dim))    */
   int causal;                  /* 0/1; bottom-right aligned when s_q > 1      */
   void* workspace;             /* device, >= mha_workspace_size bytes, 256-B aligned */
@@ -131,9 +134,10 @@ typedef struct {
  * `stream`.  Writes out and lse for every (b, i, h).
  * Alignment: q, both caches, out and workspace 16-byte aligned; every stride
  * a positive multiple of 8 elements; lse and the int32 arrays 4-byte aligned.
- * Errors: INVALID_VALUE (null pointer, non-positive size, bad stride or
- * alignment, non-finite or non-positive scale, h_q not a multiple of h_kv),
- * UNSUPPORTED (dtype, head_dim, page size), WORKSPACE_TOO_SMALL, HIP.
+ * Errors: INVALID_VALUE (null pointer, exactly one of sched / split_offsets
+ * NULL, non-positive size, bad stride or alignment, non-finite or
+ * non-positive scale, h_q not a multiple of h_kv), UNSUPPORTED (dtype,
+ * head_dim, page size), WORKSPACE_TOO_SMALL, HIP.
  */
 mla_status mha_decode(const mha_decode_args* args, hipStream_t stream);
 /* (also UNSUPPORTED: an fp8 cache with dtype other than bf16, or a kv_dtype

@@ -51,9 +51,11 @@ mla_status check_mha(const mha_decode_args* a) {
   if (st != MLA_SUCCESS) return st;
   if (a->num_pages <= 0 || a->max_pages_per_seq <= 0 || a->num_parts <= 0)
     return fail(MLA_ERROR_INVALID_VALUE, "num_pages, max_pages_per_seq and num_parts must be positive");
-  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->cache_seqlens || !a->sched ||
-      !a->split_offsets || !a->workspace || !a->out || !a->lse)
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->cache_seqlens || !a->workspace || !a->out ||
+      !a->lse)
     return fail(MLA_ERROR_INVALID_VALUE, "a required pointer is NULL");
+  if (!a->sched != !a->split_offsets)
+    return fail(MLA_ERROR_INVALID_VALUE, "sched and split_offsets must both be given or both be NULL");
   if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16) ||
       !aligned(a->workspace, 16))
     return fail(MLA_ERROR_INVALID_VALUE, "q, k_cache, v_cache, out and workspace must be 16-byte aligned");
@@ -111,6 +113,7 @@ mla::MhaParams make_mha_params(const mha_decode_args* a) {
   p.seqlens = a->cache_seqlens;
   p.sched = a->sched;
   p.split_offsets = a->split_offsets;
+  p.sched_f = MLA_FIXED_OVERHEAD;
   p.batch = a->batch; p.s_q = a->s_q; p.h_q = a->h_q; p.h_kv = a->h_kv;
   p.group = a->h_q / a->h_kv;
   p.rows = a->s_q * p.group;

@@ -34,6 +34,7 @@
 // before their bf16 rounding (the denominator sums the unscaled ones).
 #include "mla_common.hpp"
 #include "mla_internal.h"
+#include "mla_sched.hpp"
 
 namespace mla {
 
@@ -153,20 +154,21 @@ __global__ __launch_bounds__(256, 1) void mha_splitkv_kernel(MhaParams p) {
     }
   }
 
-  const int32_t* sc = p.sched + blockIdx.x * 8;
-  const int begin_u = ldu(sc + 0), begin_page = ldu(sc + 1);
-  const int end_u = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
-  for (int u = begin_u; u <= end_u; ++u) {
+  // the schedule row, precomputed or derived here
+  const PartRow pr = part_row(p.sched, p.seqlens, p.batch * p.h_kv, p.h_kv, p.num_parts, p.sched_f, blockIdx.x);
+  const int len0 = pr.len0;
+  int sched_start = pr.start, sched_slot = pr.slot;
+  for (int u = pr.begin; u <= pr.end; ++u) {
     const int b = u / p.h_kv;
     const int hk = u - b * p.h_kv;
-    const int n = ldu(p.seqlens + b);
+    const int n = (pr.inl && u == pr.begin) ? len0 : ldu(p.seqlens + b);
     const int npages = (n + kPage - 1) / kPage;
-    const int lo = (u == begin_u) ? begin_page : 0;
-    const int hi = (u == end_u) ? end_page : npages;
+    int slot0, nsplit;
+    unit_slots(pr.inl, p.split_offsets, u, n, p.sched_f, pr.width, sched_start, sched_slot, slot0, nsplit);
+    const int lo = (u == pr.begin) ? pr.begin_page : 0;
+    const int hi = (u == pr.end) ? pr.end_page : npages;
     if (lo >= hi) continue;
-    const int split = (u == begin_u) ? begin_split : 0;
-    const int slot0 = ldu(p.split_offsets + u);
-    const int nsplit = ldu(p.split_offsets + u + 1) - slot0;
+    const int split = (u == pr.begin) ? pr.begin_split : 0;
     // steps of this chunk: its pages, less trailing steps wholly past the end
     const int ks0 = lo * SPP;
     const int nsteps = (min(n, hi * kPage) - lo * kPage + KS - 1) / KS;
@@ -506,20 +508,21 @@ __global__ __launch_bounds__(256, 1) void mha_keysplit_kernel(MhaParams p) {
     doff[i] = (int)(r * rs * ESZ) + c * 16;
   }
 
-  const int32_t* sc = p.sched + blockIdx.x * 8;
-  const int begin_u = ldu(sc + 0), begin_page = ldu(sc + 1);
-  const int end_u = ldu(sc + 2), end_page = ldu(sc + 3), begin_split = ldu(sc + 4);
-  for (int u = begin_u; u <= end_u; ++u) {
+  // the schedule row, precomputed or derived here
+  const PartRow pr = part_row(p.sched, p.seqlens, p.batch * p.h_kv, p.h_kv, p.num_parts, p.sched_f, blockIdx.x);
+  const int len0 = pr.len0;
+  int sched_start = pr.start, sched_slot = pr.slot;
+  for (int u = pr.begin; u <= pr.end; ++u) {
     const int b = u / p.h_kv;
     const int hk = u - b * p.h_kv;
-    const int n = ldu(p.seqlens + b);
+    const int n = (pr.inl && u == pr.begin) ? len0 : ldu(p.seqlens + b);
     const int npages = (n + kPage - 1) / kPage;
-    const int lo = (u == begin_u) ? begin_page : 0;
-    const int hi = (u == end_u) ? end_page : npages;
+    int slot0, nsplit;
+    unit_slots(pr.inl, p.split_offsets, u, n, p.sched_f, pr.width, sched_start, sched_slot, slot0, nsplit);
+    const int lo = (u == pr.begin) ? pr.begin_page : 0;
+    const int hi = (u == pr.end) ? pr.end_page : npages;
     if (lo >= hi) continue;
-    const int split = (u == begin_u) ? begin_split : 0;
-    const int slot0 = ldu(p.split_offsets + u);
-    const int nsplit = ldu(p.split_offsets + u + 1) - slot0;
+    const int split = (u == pr.begin) ? pr.begin_split : 0;
     const int nsteps = hi - lo;              // one step per page
 
     BlockWindow bw;
@@ -810,8 +813,16 @@ __global__ __launch_bounds__(256) void mha_combine_kernel(MhaParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + wave;
   if (row >= p.rows) return;
-  const int s0 = ldu(p.split_offsets + u);
-  const int ns = ldu(p.split_offsets + u + 1) - s0;
+  int s0, ns;
+  if (p.split_offsets) {
+    s0 = ldu(p.split_offsets + u);
+    ns = ldu(p.split_offsets + u + 1) - s0;
+  } else {                                       // the schedule derived in place
+    int before, own;
+    sched_slots(p.seqlens, p.batch * p.h_kv, p.h_kv, p.num_parts, p.sched_f, u, before, own);
+    s0 = __builtin_amdgcn_readfirstlane(before);   // lane 0 holds unit u
+    ns = __builtin_amdgcn_readfirstlane(own);
+  }
   if (ns == 1) return;
   const int b = u / p.h_kv, hk = u - b * p.h_kv;
   const int tok = row / p.group;

@@ -78,8 +78,9 @@ struct MhaParams {
   const int32_t* block_table;
   int64_t bt_s;
   const int32_t* seqlens;
-  const int32_t* sched;
-  const int32_t* split_offsets;
+  const int32_t* sched;          // null: every wave derives the schedule from seqlens
+  const int32_t* split_offsets;  // null exactly when sched is
+  int sched_f;                   // the scheduler's per-piece overhead F (pages)
   int batch, s_q, h_q, h_kv, group, rows, num_parts, causal;
   float scale_log2;         // softmax_scale * log2(e)
   void* out;

@@ -64,15 +64,16 @@ __device__ __forceinline__ int at_last(int v, uint64_t mask) {
   return __builtin_amdgcn_readlane(v, 63 - __builtin_clzll(mask));
 }
 
-// Unit lengths are read 256 at a time (four per lane, all loads issued
-// before any is used).
-constexpr int kSchedBlock = 256;
+// Unit lengths are read 512 at a time (eight per lane, all loads issued
+// before any is used): up to 512 units, one memory round trip.
+constexpr int kSchedPer = 8;
+constexpr int kSchedBlock = 64 * kSchedPer;
 
 __device__ __forceinline__ void sched_load_block(const int32_t* seqlens, int units, int rep, int u0,
-                                                 int (&n)[4]) {
+                                                 int (&n)[kSchedPer]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kSchedPer; ++j) {
     const int u = u0 + j * 64 + lane;
     n[j] = u < units ? seqlens[u / rep] : 0;
   }
@@ -81,11 +82,11 @@ __device__ __forceinline__ void sched_load_block(const int32_t* seqlens, int uni
 __device__ __forceinline__ int sched_total(const int32_t* seqlens, int units, int rep, int F) {
   int total = 0;
   for (int u0 = 0; u0 < units; u0 += kSchedBlock) {
-    int n[4];
+    int n[kSchedPer];
     sched_load_block(seqlens, units, rep, u0, n);
     int c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c += sched_cost(n[j], F);
+    for (int j = 0; j < kSchedPer; ++j) c += sched_cost(n[j], F);
     total += wave_total(c);
   }
   return total;
@@ -104,13 +105,13 @@ __device__ __forceinline__ SchedRow sched_row(const int32_t* seqlens, int units,
   SchedRow r = {0, 0, -1, 0, 0, 0, 0, 0, 1};
   // up to kSchedBlock units the lengths are read once and stay in registers
   const bool one = units <= kSchedBlock;
-  int first[4];
+  int first[kSchedPer];
   if (one) sched_load_block(seqlens, units, rep, 0, first);
   int total;
   if (one) {
     int c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c += sched_cost(first[j], F);
+    for (int j = 0; j < kSchedPer; ++j) c += sched_cost(first[j], F);
     total = wave_total(c);
   } else {
     total = sched_total(seqlens, units, rep, F);
@@ -127,32 +128,33 @@ __device__ __forceinline__ SchedRow sched_row(const int32_t* seqlens, int units,
   // s, e - 1 and e - 1 - F
   int run = 0, slot = 0, n_s = 0, n_e = 0, n_f = 0, c_s = 0, c_e = 0, c_f = 0, len_s = 0;
   for (int u0 = 0; u0 < units; u0 += kSchedBlock) {
-    int n[4];
+    int n[kSchedPer];
     if (one) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) n[j] = first[j];
+      for (int j = 0; j < kSchedPer; ++j) n[j] = first[j];
     } else {
       sched_load_block(seqlens, units, rep, u0, n);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (u0 + j * 64 >= units) break;            // no unit left in this or later blocks
-      const bool in = u0 + j * 64 + lane < units;
-      const int c = sched_cost(n[j], F);
-      const int incl = wave_inclusive_sum(c);
-      const int C = run + incl - c;
-      const int pc = sched_pieces(C, c, F, width, rw);
-      slot += wave_total(C + c <= s32 ? pc : 0);
-      const uint64_t ms = __ballot(in && C <= s32);
-      const uint64_t me = __ballot(in && C <= e - 1);
-      const uint64_t mf = __ballot(in && C <= e - 1 - F);
-      if (ms) { c_s = at_last(C, ms); len_s = at_last(n[j], ms); }
-      if (me) c_e = at_last(C, me);
-      if (mf) c_f = at_last(C, mf);
-      n_s += count_of(ms);
-      n_e += count_of(me);
-      n_f += count_of(mf);
-      run += __builtin_amdgcn_readlane(incl, 63);
+    for (int j = 0; j < kSchedPer; ++j) {
+      if (u0 + j * 64 < units) {                  // blocks past the last unit hold nothing
+        const bool in = u0 + j * 64 + lane < units;
+        const int c = sched_cost(n[j], F);
+        const int incl = wave_inclusive_sum(c);
+        const int C = run + incl - c;
+        const int pc = sched_pieces(C, c, F, width, rw);
+        slot += wave_total(C + c <= s32 ? pc : 0);
+        const uint64_t ms = __ballot(in && C <= s32);
+        const uint64_t me = __ballot(in && C <= e - 1);
+        const uint64_t mf = __ballot(in && C <= e - 1 - F);
+        if (ms) { c_s = at_last(C, ms); len_s = at_last(n[j], ms); }
+        if (me) c_e = at_last(C, me);
+        if (mf) c_f = at_last(C, mf);
+        n_s += count_of(ms);
+        n_e += count_of(me);
+        n_f += count_of(mf);
+        run += __builtin_amdgcn_readlane(incl, 63);
+      }
     }
   }
   if (c_s + F >= e) return r;                 // only the overhead of a piece falls here
@@ -181,11 +183,11 @@ __device__ __forceinline__ void sched_slots(const int32_t* seqlens, int units, i
   const int lane = threadIdx.x & 63;
   if (units <= kSchedBlock) {
     // one load round: all lengths in registers, unit j * 64 + lane in n[j]
-    int n[4];
+    int n[kSchedPer];
     sched_load_block(seqlens, units, rep, 0, n);
-    int c[4], t = 0;
+    int c[kSchedPer], t = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSchedPer; ++j) {
       c[j] = sched_cost(n[j], F);
       t += c[j];
     }
@@ -194,21 +196,22 @@ __device__ __forceinline__ void sched_slots(const int32_t* seqlens, int units, i
     const double rw = 1.0 / width;
     int run = 0, slot = 0, got_before = 0, got_own = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j * 64 >= units) break;                 // no unit left in this or later blocks
-      const int incl = wave_inclusive_sum(c[j]);
-      const int pc = sched_pieces(run + incl - c[j], c[j], F, width, rw);
-      const int pincl = wave_inclusive_sum(pc);
-      // the window's lanes: unit u0 + lane sits in block j at lane (u0 + lane) - 64 j
-      const int src = u0 + lane - 64 * j;
-      const int bj = __builtin_amdgcn_ds_bpermute(max(0, min(63, src)) << 2, slot + pincl - pc);
-      const int oj = __builtin_amdgcn_ds_bpermute(max(0, min(63, src)) << 2, pc);
-      if (src >= 0 && src < 64) {
-        got_before = bj;
-        got_own = oj;
+    for (int j = 0; j < kSchedPer; ++j) {
+      if (j * 64 < units) {                       // blocks past the last unit hold nothing
+        const int incl = wave_inclusive_sum(c[j]);
+        const int pc = sched_pieces(run + incl - c[j], c[j], F, width, rw);
+        const int pincl = wave_inclusive_sum(pc);
+        // the window's lanes: unit u0 + lane sits in block j at lane (u0 + lane) - 64 j
+        const int src = u0 + lane - 64 * j;
+        const int bj = __builtin_amdgcn_ds_bpermute(max(0, min(63, src)) << 2, slot + pincl - pc);
+        const int oj = __builtin_amdgcn_ds_bpermute(max(0, min(63, src)) << 2, pc);
+        if (src >= 0 && src < 64) {
+          got_before = bj;
+          got_own = oj;
+        }
+        slot += __builtin_amdgcn_readlane(pincl, 63);
+        run += __builtin_amdgcn_readlane(incl, 63);
       }
-      slot += __builtin_amdgcn_readlane(pincl, 63);
-      run += __builtin_amdgcn_readlane(incl, 63);
     }
     // units >= `units` (the lane of index `units` included) have no pieces
     // and sit after every piece: before = the total count
@@ -223,10 +226,10 @@ __device__ __forceinline__ void sched_slots(const int32_t* seqlens, int units, i
   const int head = min(u0, units);              // units wholly ahead of the window
   int run = 0, slot = 0;
   for (int v0 = 0; v0 < head; v0 += kSchedBlock) {
-    int n[4];
+    int n[kSchedPer];
     sched_load_block(seqlens, head, rep, v0, n);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSchedPer; ++j) {
       const int c = sched_cost(n[j], F);
       const int incl = wave_inclusive_sum(c);
       slot += wave_total(sched_pieces(run + incl - c, c, F, width, rw));
@@ -238,6 +241,56 @@ __device__ __forceinline__ void sched_slots(const int32_t* seqlens, int units, i
   const int incl = wave_inclusive_sum(c);
   own = sched_pieces(run + incl - c, c, F, width, rw);
   before = slot + wave_inclusive_sum(own) - own;
+}
+
+// The row of one partition, for a kernel that takes the schedule either
+// precomputed (a row of `sched`) or derived in place (sched == nullptr): its
+// units run from `begin` (from page begin_page, first piece begin_split) to
+// `end` (up to page end_page).  Derived in place, it also carries the walk's
+// starting state: C and the first slot of unit `begin`, that unit's length,
+// and the width (see unit_slots).
+struct PartRow {
+  int begin, begin_page, end, end_page, begin_split, inl, start, slot, len0, width;
+};
+
+__device__ __forceinline__ PartRow part_row(const int32_t* sched, const int32_t* seqlens, int units, int rep,
+                                            int parts, int F, int k) {
+  PartRow w;
+  w.inl = sched == nullptr;
+  if (w.inl) {
+    const SchedRow r = sched_row(seqlens, units, rep, parts, F, k);
+    w.begin = r.b0; w.begin_page = r.p0; w.end = r.b1; w.end_page = r.p1; w.begin_split = r.split0;
+    w.start = r.c0; w.slot = r.slot0; w.len0 = r.n0; w.width = r.width;
+  } else {
+    const int32_t* sc = sched + k * 8;
+    w.begin = ldu(sc + 0); w.begin_page = ldu(sc + 1);
+    w.end = ldu(sc + 2); w.end_page = ldu(sc + 3); w.begin_split = ldu(sc + 4);
+    w.start = w.slot = w.len0 = 0;
+    w.width = 1;
+  }
+  return w;
+}
+
+// First piece slot and piece count of unit u with length n.  Derived in
+// place, the units must be visited in order from the row's first one (also
+// those the partition holds no page of), carrying `start` (C of the unit) and
+// `slot` (its first slot) from one to the next; the kernel keeps both in
+// plain scalars: a member read selected against a load would give the walk's
+// state an address and put it in scratch memory.
+__device__ __forceinline__ void unit_slots(int inl, const int32_t* split_offsets, int u, int n, int F, int width,
+                                           int& start, int& slot, int& slot0, int& nsplit) {
+  if (inl) {
+    const int cost = sched_cost(n, F);
+    const int ns = sched_pieces(start, cost, F, width, 1.0 / width);
+    slot0 = slot;
+    nsplit = ns;
+    start += cost;
+    slot += ns;
+  } else {
+    const int s0 = ldu(split_offsets + u);
+    slot0 = s0;
+    nsplit = ldu(split_offsets + u + 1) - s0;
+  }
 }
 
 }  // namespace mla

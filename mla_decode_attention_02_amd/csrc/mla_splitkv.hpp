@@ -67,37 +67,19 @@ struct Chunk {
 // request lengths.
 template <typename F>
 __device__ __forceinline__ void for_each_chunk(const DecodeParams& p, F&& f) {
-  int begin_req, begin_page, end_req, end_page, begin_split;
-  int start = 0, slot = 0, len0 = 0, width = 1;
-  const bool inl = p.sched == nullptr;
-  if (inl) {
-    const SchedRow r = sched_row(p.seqlens, p.batch, 1, p.num_parts, p.sched_f, blockIdx.x);
-    begin_req = r.b0; begin_page = r.p0; end_req = r.b1; end_page = r.p1; begin_split = r.split0;
-    start = r.c0; slot = r.slot0; len0 = r.n0; width = r.width;
-  } else {
-    const int32_t* sc = p.sched + blockIdx.x * 8;
-    begin_req = ldu(sc + 0); begin_page = ldu(sc + 1);
-    end_req = ldu(sc + 2); end_page = ldu(sc + 3); begin_split = ldu(sc + 4);
-  }
-  for (int b = begin_req; b <= end_req; ++b) {
+  const PartRow r = part_row(p.sched, p.seqlens, p.batch, 1, p.num_parts, p.sched_f, blockIdx.x);
+  const int len0 = r.len0;
+  int start = r.start, slot = r.slot;
+  for (int b = r.begin; b <= r.end; ++b) {
     Chunk c;
     c.b = b;
-    c.n = (inl && b == begin_req) ? len0 : ldu(p.seqlens + b);
+    c.n = (r.inl && b == r.begin) ? len0 : ldu(p.seqlens + b);
     const int npages = (c.n + kPage - 1) / kPage;
-    if (inl) {
-      const int cost = sched_cost(c.n, p.sched_f);
-      c.slot0 = slot;
-      c.nsplit = sched_pieces(start, cost, p.sched_f, width, 1.0 / width);
-      start += cost;
-      slot += c.nsplit;
-    } else {
-      c.slot0 = ldu(p.split_offsets + b);
-      c.nsplit = ldu(p.split_offsets + b + 1) - c.slot0;
-    }
-    c.lo = (b == begin_req) ? begin_page : 0;
-    c.hi = (b == end_req) ? end_page : npages;
+    unit_slots(r.inl, p.split_offsets, b, c.n, p.sched_f, r.width, start, slot, c.slot0, c.nsplit);
+    c.lo = (b == r.begin) ? r.begin_page : 0;
+    c.hi = (b == r.end) ? r.end_page : npages;
     if (c.lo >= c.hi) continue;
-    c.split = (b == begin_req) ? begin_split : 0;
+    c.split = (b == r.begin) ? r.begin_split : 0;
     f(c);
   }
 }
