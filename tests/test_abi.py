@@ -322,6 +322,8 @@ MHA_BREAKS = [
     ("batch", lambda a: setattr(a, "batch", 0), INVALID),
     ("num_parts", lambda a: setattr(a, "num_parts", 0), INVALID),
     ("v null", lambda a: setattr(a, "v_cache", None), INVALID),
+    ("sched null alone", lambda a: setattr(a, "sched", None), INVALID),
+    ("split_offsets null alone", lambda a: setattr(a, "split_offsets", None), INVALID),
     ("v misaligned", lambda a: setattr(a, "v_cache", 3 * (1 << 20) + 8), INVALID),
     ("k stride", lambda a: a.k_stride.__setitem__(1, 100), INVALID),
     ("slot stride small", lambda a: a.v_stride.__setitem__(1, 128), INVALID),
