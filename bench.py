@@ -228,7 +228,7 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
              "Commands (from the repository root on one MI355X, TMPDIR=/tmp):", "",
              "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{tag} -o {tag} -- "
-             f"python3 bench.py --workload {workload} --steps 20 --warmup 5 --no-cpu-baseline{ref}",
+             f"python3 bench.py --workload {workload} --steps 100 --warmup 20 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf_{tag} -o p -- "
              f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_{tag} -o p -- "
