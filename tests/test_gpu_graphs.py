@@ -126,3 +126,41 @@ def test_mha_fp8_graph_replay():
                               k_scale=x.k_scale, v_scale=x.v_scale)
 
     _replays_match(run, eager)
+
+
+@pytest.mark.parametrize("entry", ["mla_decode", "mla_decode_fused"])
+@pytest.mark.parametrize("h_q,kv", [(16, "same"), (128, "same"), (16, "fp8")])
+def test_mla_graph_replay_schedule_in_kernels(entry, h_q, kv):
+    # no schedule passed: the graph holds only the split-KV kernel and the
+    # combine, both deriving the schedule from cache_seqlens on every replay
+    _say(f"graph replay {entry} h_q={h_q} kv={kv}, schedule in the kernels")
+    x = make_inputs(4, 1, h_q, "bf16", seqlens=(900, 33, 2000, 1), seed=65, kv_dtype=kv).to(torch.device("cuda:0"))
+    parts = 17
+    fn = getattr(api, entry)
+    o, l = fn(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, False, metadata=parts,
+              buffers=api.DecodeBuffers(x.q, parts), k_scale=x.k_scale)
+    torch.cuda.synchronize()
+    eager = (o.clone(), l.clone())
+    gbufs = api.DecodeBuffers(x.q, parts)
+
+    def run():
+        return fn(x.q, x.k_cache, x.block_table, x.cache_seqlens, x.softmax_scale, False, metadata=parts,
+                  buffers=gbufs, k_scale=x.k_scale)
+
+    _replays_match(run, eager)
+
+
+def test_mha_graph_replay_schedule_in_kernels():
+    _say("graph replay MHA, schedule in the kernels")
+    x = make_mha_inputs(3, 1, 16, 4, 128, "bf16", seqlens=(1500, 64, 7), seed=66).to(torch.device("cuda:0"))
+    o, l = api.mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, metadata=11,
+                          buffers=api.MhaBuffers(x.q, 4, 11))
+    torch.cuda.synchronize()
+    eager = (o.clone(), l.clone())
+    gbufs = api.MhaBuffers(x.q, 4, 11)
+
+    def run():
+        return api.mha_decode(x.q, x.k_cache, x.v_cache, x.block_table, x.cache_seqlens, metadata=11,
+                              buffers=gbufs)
+
+    _replays_match(run, eager)
