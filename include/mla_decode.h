@@ -173,10 +173,12 @@ mla_status mla_get_metadata_ex(const int32_t* cache_seqlens, int batch, int s_q,
  * "辅助优化：可编程依赖启动与瓦片调度": split-KV work, then a combine kernel),
  * so each piece's fp32 output and LSE are parked here.  Layout: first the arrival
  * counters of mla_decode_fused (m_blocks * batch int32, rounded up to 256 bytes;
- * m_blocks = ceil(s_q*h_q / 64), or 1 when s_q*h_q <= 16), then fp32 partial
- * outputs and LSEs for up to (batch + num_parts) request pieces of s_q*h_q
- * rows each ((batch + num_parts) * s_q * h_q * (512 + 1) * 4 bytes, rounded up
- * to 256).
+ * m_blocks = ceil(s_q*h_q / 64), or 1 when s_q*h_q <= 16), then each
+ * request's first piece slot and piece count (batch * 2 int32, rounded up to
+ * 256 bytes; written by the split-KV kernel for the combine when the call
+ * passes no schedule), then fp32 partial outputs and LSEs for up to
+ * (batch + num_parts) request pieces of s_q*h_q rows each
+ * ((batch + num_parts) * s_q * h_q * (512 + 1) * 4 bytes, rounded up to 256).
  * Errors: INVALID_VALUE.
  */
 mla_status mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes);

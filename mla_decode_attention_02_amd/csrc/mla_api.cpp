@@ -79,9 +79,11 @@ mla_status check_shape(int batch, int s_q, int h_q, int h_kv) {
 }
 
 // Workspace: the arrival counters of the fused merge [m_blocks, batch] int32
-// first (their place depends on the shape only, not on num_parts), then fp32
-// partial outputs [slots, rows, 512] and their LSEs [slots, rows]; each region
-// starts on a 256-byte boundary.
+// first (their place depends on the shape only, not on num_parts), then each
+// request's first piece slot and piece count [batch][2] int32 (written when
+// the kernels derive the schedule themselves), then fp32 partial outputs
+// [slots, rows, 512] and their LSEs [slots, rows]; each region starts on a
+// 256-byte boundary.
 
 size_t counters_bytes(int batch, int s_q, int h_q) {
   const int rows = s_q * h_q;
@@ -89,10 +91,13 @@ size_t counters_bytes(int batch, int s_q, int h_q) {
   return round256(m_blocks * (size_t)batch * sizeof(int32_t));
 }
 
+size_t req_slots_bytes(int batch) { return round256((size_t)batch * 2 * sizeof(int32_t)); }
+
 size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
   const size_t slots = (size_t)batch + (size_t)num_parts;
   const size_t rows = (size_t)s_q * h_q;
-  return counters_bytes(batch, s_q, h_q) + round256(slots * rows * (mla::kDV + 1) * sizeof(float));
+  return counters_bytes(batch, s_q, h_q) + req_slots_bytes(batch) +
+         round256(slots * rows * (mla::kDV + 1) * sizeof(float));
 }
 
 mla_status check_decode(const mla_decode_args* a) {
@@ -174,7 +179,9 @@ mla::DecodeParams make_params(const mla_decode_args* a) {
   p.lse = a->lse;
   const size_t slots = (size_t)a->batch + (size_t)a->num_parts;
   p.counters = static_cast<int*>(a->workspace);
-  p.part_o = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + counters_bytes(a->batch, a->s_q, a->h_q));
+  char* ws = static_cast<char*>(a->workspace) + counters_bytes(a->batch, a->s_q, a->h_q);
+  p.req_slots = reinterpret_cast<int*>(ws);
+  p.part_o = reinterpret_cast<float*>(ws + req_slots_bytes(a->batch));
   p.part_lse = p.part_o + slots * (size_t)p.rows * mla::kDV;
   p.fuse_max = 0;
   return p;

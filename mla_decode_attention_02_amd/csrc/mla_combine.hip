@@ -50,10 +50,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     s0 = ldu(p.split_offsets + b);
     ns = ldu(p.split_offsets + b + 1) - s0;
   } else {
-    int before, own;
-    sched_slots(p.seqlens, p.batch, 1, p.num_parts, p.sched_f, b, before, own);
-    s0 = __builtin_amdgcn_readfirstlane(before);                    // lane 0 holds request b
-    ns = __builtin_amdgcn_readfirstlane(own);
+    // the split-KV kernel recorded them, for every request with a page
+    const int n = ldu(p.seqlens + b);
+    s0 = ldu(p.req_slots + 2 * b);
+    const int rec_ns = ldu(p.req_slots + 2 * b + 1);
+    ns = n > 0 ? rec_ns : 0;
   }
   if (ns == 1 || (ns > 1 && ns <= p.fuse_max)) return;   // whole, or merged by the split-KV kernel
   const float* lse_k = p.part_lse + (int64_t)s0 * p.rows + row;   // stride p.rows per piece

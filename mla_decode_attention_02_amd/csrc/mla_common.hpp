@@ -60,6 +60,9 @@ struct DecodeParams {
   int kv_fp8;               // k_cache holds fp8 e4m3 codes (else the dtype of q)
   const float* k_scale;     // fp8: per-page scale (K = code * scale), or null for 1
   int* counters;            // [m_blocks, batch] arrivals per row tile of a split request
+  int* req_slots;           // [batch][2] first piece slot and piece count per request,
+                            // written by the split-KV kernel when it derives the
+                            // schedule itself, read by the combine
   int fuse_max;             // requests cut into 2 .. fuse_max pieces are merged in the
                             // split-KV kernel (0: never)
 };

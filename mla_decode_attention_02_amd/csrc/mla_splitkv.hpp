@@ -80,6 +80,9 @@ __device__ __forceinline__ void for_each_chunk(const DecodeParams& p, F&& f) {
     c.hi = (b == r.end) ? r.end_page : npages;
     if (c.lo >= c.hi) continue;
     c.split = (b == r.begin) ? r.begin_split : 0;
+    // the piece that starts a request records its slots for the combine
+    if (r.inl && c.split == 0 && threadIdx.x == 0 && blockIdx.y == 0)
+      *(u32x2*)(p.req_slots + 2 * b) = u32x2{(uint32_t)c.slot0, (uint32_t)c.nsplit};
     f(c);
   }
 }

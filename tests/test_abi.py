@@ -58,11 +58,13 @@ def test_workspace_size_formula(L):
     for batch, s_q, h_q, parts in ((2, 1, 16, 256), (64, 1, 128, 128), (32, 2, 128, 64), (1, 1, 1, 1)):
         n = api.workspace_size(batch, s_q, h_q, parts)
         # the fused path's counters (one per request and 64-row tile, or per
-        # request when s_q*h_q <= 16), then partials and LSEs
+        # request when s_q*h_q <= 16), the per-request slot records, then
+        # partials and LSEs
         raw = (batch + parts) * s_q * h_q * 513 * 4
         rows = s_q * h_q
         m_blocks = 1 if rows <= 16 else (rows + 63) // 64
-        assert n == (raw + 255) // 256 * 256 + (m_blocks * batch * 4 + 255) // 256 * 256
+        r256 = lambda x: (x + 255) // 256 * 256
+        assert n == r256(raw) + r256(m_blocks * batch * 4) + r256(batch * 8)
 
 
 def test_metadata_shape_with_explicit_cu_count(L):
