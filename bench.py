@@ -340,18 +340,21 @@ def bench_mha(args) -> dict:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = HipEvents(2 * args.steps)               # around the split-KV kernel of every step
+    # events around the split-KV kernel of every EVENT_STRIDE-th timed step
+    sampled = list(range(0, args.steps, max(1, min(EVENT_STRIDE, args.steps // 10))))
+    slot = {i: 2 * j for j, i in enumerate(sampled)}
+    ev = HipEvents(2 * len(sampled))
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(args.steps):
-        step(args.warmup + i, (ev, 2 * i))
+        step(args.warmup + i, (ev, slot[i]) if i in slot else None)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = max(t0.elapsed_time(t1), wall * 1e3) / args.steps
-    ks = sorted(ev.ms(2 * i, 2 * i + 1) for i in range(args.steps))
+    ks = sorted(ev.ms(b, b + 1) for b in slot.values())
     ev.close()
     kavg = sum(ks) / len(ks)
     ach = splitkv_bytes / (kavg * 1e-3) / 1e9
@@ -404,6 +407,11 @@ def bench_mha(args) -> dict:
                                   "sample": f"{done} whole requests of the same workload, fp64 NumPy, {dt:.1f} s"}
         result["parity_vs_oracle"] = {"requests": done, "max_abs_dO": dO, "max_abs_dLSE": dL}
     return result
+
+
+# Timed steps bracketed by events: one in EVENT_STRIDE (the kernel and step
+# medians come from these samples; the rest of the timed region runs bare).
+EVENT_STRIDE = 10
 
 
 class HipEvents:
@@ -509,8 +517,8 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     (copies >= 2 and a cache larger than the last-level caches: every step
     reads its pages from HBM).  The same steps with the schedule precomputed
     by mla_get_metadata (three launches) are timed after them for reference.
-    Each phase is bracketed by HIP events on the stream the library launches
-    on (torch's current stream).  Returns per-step lists (ms) and the outputs
+    One timed step in EVENT_STRIDE has its phases bracketed by HIP events on
+    the stream the library launches on (torch's current stream).  Returns per-step lists (ms) and the outputs
     of the last step."""
     import threading
 
@@ -531,8 +539,8 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
 
     def step(i, ev=None, precomputed=False):
         """One step; with `ev` = (events, base) it records events base + 0
-        (start), + 1 (after the schedule, precomputed form only) and + 2
-        (after the split-KV kernel)."""
+        (start), + 1 (after the schedule, precomputed form only), + 2 (after
+        the split-KV kernel) and + 3 (after the combine)."""
         if ev is not None:
             ev[0].record(ev[1])
         if precomputed:
@@ -548,30 +556,34 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
             ev[0].record(ev[1] + 2)
         api.mla_decode_combine(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
                                g.k_scale)
+        if ev is not None:
+            ev[0].record(ev[1] + 3)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: two events per step (start, after split-KV); a step ends
-    # where the next one starts, the last one at an end event
-    ev = HipEvents(3 * steps + 1)
+    # timed region: every EVENT_STRIDE-th step is bracketed by events (start,
+    # after split-KV, after combine); the others run without any, so the
+    # region's time per step carries almost no timing overhead
+    sampled = list(range(0, steps, max(1, min(EVENT_STRIDE, steps // 10))))
+    ev = HipEvents(4 * len(sampled))
+    slot = {i: 4 * j for j, i in enumerate(sampled)}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        step(warmup + i, (ev, 3 * i))
-    ev.record(3 * steps)
+        step(warmup + i, (ev, slot[i]) if i in slot else None)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    nxt = [3 * (i + 1) for i in range(steps)]
     res = {
         "workload": w, "host": host, "num_parts": num_parts, "fixed_overhead": F, "copies": len(caches),
         "region_ms": max(t_start.elapsed_time(t_end), wall * 1e3),
-        "splitkv_ms": [ev.ms(3 * i, 3 * i + 2) for i in range(steps)],
-        "combine_ms": [ev.ms(3 * i + 2, nxt[i]) for i in range(steps)],
-        "step_ms": [ev.ms(3 * i, nxt[i]) for i in range(steps)],
+        "splitkv_ms": [ev.ms(b, b + 2) for b in slot.values()],
+        "combine_ms": [ev.ms(b + 2, b + 3) for b in slot.values()],
+        "step_ms": [ev.ms(b, b + 3) for b in slot.values()],
+        "events_every": len(sampled) and steps // len(sampled),
         "out": bufs.out.float().cpu(), "lse": bufs.lse.cpu(),
     }
     ev.close()
@@ -579,14 +591,13 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     res["meta_ms"] = res["pre_step_ms"] = res["pre_splitkv_ms"] = None
     n_pre = max(1, min(steps, 50)) if reference else 0
     if n_pre:
-        ev = HipEvents(3 * n_pre + 1)
+        ev = HipEvents(4 * n_pre)
         for i in range(n_pre):
-            step(warmup + steps + i, (ev, 3 * i), precomputed=True)
-        ev.record(3 * n_pre)
+            step(warmup + steps + i, (ev, 4 * i), precomputed=True)
         torch.cuda.synchronize()
-        res["meta_ms"] = [ev.ms(3 * i, 3 * i + 1) for i in range(n_pre)]
-        res["pre_step_ms"] = [ev.ms(3 * i, 3 * i + 3) for i in range(n_pre)]
-        res["pre_splitkv_ms"] = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(n_pre)]
+        res["meta_ms"] = [ev.ms(4 * i, 4 * i + 1) for i in range(n_pre)]
+        res["pre_step_ms"] = [ev.ms(4 * i, 4 * i + 3) for i in range(n_pre)]
+        res["pre_splitkv_ms"] = [ev.ms(4 * i + 1, 4 * i + 2) for i in range(n_pre)]
         ev.close()
     if clock_probe:
         # sample the shader clock while the same steps keep the GPU busy
