@@ -579,7 +579,7 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
     wall = time.perf_counter() - wall0
     res = {
         "workload": w, "host": host, "num_parts": num_parts, "fixed_overhead": F, "copies": len(caches),
-        "region_ms": max(t_start.elapsed_time(t_end), wall * 1e3),
+        "region_ms": max(t_start.elapsed_time(t_end), wall * 1e3), "steps": steps,
         "splitkv_ms": [ev.ms(b, b + 2) for b in slot.values()],
         "combine_ms": [ev.ms(b + 2, b + 3) for b in slot.values()],
         "step_ms": [ev.ms(b, b + 3) for b in slot.values()],
@@ -631,7 +631,7 @@ def mla_record(idx: int, m: dict, warm: dict) -> dict:
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     bound = "hbm" if flops / step_bytes < ridge else "mfma"
     st, sk = _quantiles(m["step_ms"]), _quantiles(m["splitkv_ms"])
-    ms_step = m["region_ms"] / len(m["step_ms"])
+    ms_step = m["region_ms"] / m["steps"]
     kv_med_s = sk["median"] * 1e-3        # seconds
     rec = {
         "config": idx, "workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "dtype": w.dtype,

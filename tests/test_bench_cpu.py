@@ -81,3 +81,26 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_mla_record_rates_use_the_timed_step_count():
+    # the region is divided by the steps timed, not by the number of steps
+    # that carried timing events (one in EVENT_STRIDE)
+    import types
+
+    import torch
+
+    from mla_decode_attention_02_amd.workloads import WORKLOADS, workload_seqlens
+
+    w = WORKLOADS[2]
+    steps = 200
+    sampled = steps // bench.EVENT_STRIDE
+    m = {"workload": w, "host": types.SimpleNamespace(cache_seqlens=torch.tensor(workload_seqlens(2))),
+         "num_parts": 128, "fixed_overhead": 2, "copies": 2, "steps": steps,
+         "region_ms": steps * 0.1, "step_ms": [0.099] * sampled, "splitkv_ms": [0.09] * sampled,
+         "combine_ms": [0.009] * sampled, "meta_ms": None, "pre_step_ms": None, "pre_splitkv_ms": None}
+    rec = bench.mla_record(2, m, {"step_ms": [0.098] * 5})
+    assert rec["ms_per_step_region"] == 0.1
+    flops = bench.algorithmic_counts(workload_seqlens(2), w.batch, w.s_q, w.h_q)[0]
+    assert abs(rec["step_tflops"] - flops / 1e-4 / 1e12) < 0.01
+    assert rec["splitkv_us"]["median"] == 90.0 and rec["metadata_us_median"] is None
