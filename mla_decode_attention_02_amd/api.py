@@ -313,11 +313,12 @@ class DecodeBuffers:
         self.workspace = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
 
 
-# Batches up to this many requests derive the schedule inside the kernels by
-# default: each workgroup's scan of the request lengths costs ~0.5 us per 64
-# requests at kernel start, against a metadata launch (measured on MI355X:
-# neutral to 1.2 us per step faster at 64-128 requests, 4.5 us slower at 512
-# units of the MHA path).
+# MLA batches up to this many requests derive the schedule inside the kernels
+# by default: each workgroup's scan of the request lengths costs ~0.5 us per
+# 64 requests at kernel start, against a metadata launch (measured on MI355X:
+# neutral to 1.2 us per step faster at 64-128 requests).  The MHA path keeps
+# the metadata launch by default: its kernels measured slower with the scan
+# (1.4 us at 128 units, 4.5 us at 512).
 INLINE_SCHEDULE_MAX_UNITS = 256
 
 
@@ -541,17 +542,13 @@ def _mha_call(fn_name, q, k_cache, v_cache, block_table, cache_seqlens, softmax_
     _validate_mha(q, k_cache, v_cache, block_table, cache_seqlens, k_scale, v_scale)
     B, s_q, h_q, d = q.shape
     h_kv = k_cache.shape[2]
-    if metadata is None and B * h_kv > INLINE_SCHEDULE_MAX_UNITS:
+    if metadata is None:
         metadata = mha_get_metadata(cache_seqlens, s_q, h_q, h_kv)
-    if metadata is None or isinstance(metadata, int):
-        # no schedule passed: the kernels derive it from cache_seqlens
-        if metadata is None:
-            with torch.cuda.device(q.device):
-                parts = mha_get_metadata_shape(B, s_q, h_q, h_kv)[0]
-        else:
-            parts = int(metadata)
-            if parts <= 0:
-                raise ValueError("the number of partitions must be positive")
+    if isinstance(metadata, int):
+        # a partition count: the kernels derive the schedule from cache_seqlens
+        parts = int(metadata)
+        if parts <= 0:
+            raise ValueError("the number of partitions must be positive")
         sched = offs = None
     else:
         sched, offs = metadata
@@ -601,10 +598,10 @@ def mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, bl
     Returns (out [B, s_q, h_q, d] in q's dtype, lse [B, s_q, h_q] fp32).
     softmax_scale defaults to 1/sqrt(d).  fp8 caches (torch.float8_e4m3fn, bf16
     q) take optional fp32 scales k_scale / v_scale [num_pages, h_kv].
-    `metadata` is mha_get_metadata's result, or a partition count: the
-    kernels then derive the schedule themselves; None (the default) does that
-    for up to INLINE_SCHEDULE_MAX_UNITS (request, KV head) units and calls
-    mha_get_metadata beyond."""
+    `metadata` is mha_get_metadata's result (computed here when None, the
+    default), or a partition count: the kernels then derive the schedule
+    themselves (measured slower on this path than the metadata launch, by
+    1.4 us at 128 units and 4.5 us at 512)."""
     if softmax_scale is None:
         softmax_scale = q.shape[-1] ** -0.5
     return _mha_call("mha_decode", q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal,
