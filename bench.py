@@ -26,7 +26,8 @@ every request).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
 --workload N times one workload alone: 1-5 as above, 6, 11 and 12 the fp8-cache
-variants of 3, 2 and 5, and 7-10 the paged grouped-query (MHA) path (schedule
+variants of 3, 2 and 5, 13 and 14 those of 2 and 5 with the fp8 query-key
+product as well, and 7-10 the paged grouped-query (MHA) path (schedule
 mha_get_metadata, split-KV kernel and combine over separate K and V caches).
 """
 
@@ -64,7 +65,7 @@ KERNEL_SOURCES = {
 def mla_kernel_name(w) -> str:
     """The split-KV kernel that runs a workload."""
     if w.kv == "fp8":
-        return "splitkv_wide_fp8_kernel" if w.rows > 16 else "splitkv_fp8_kernel"
+        return "splitkv_wide_fp8_kernel" if w.rows > 16 or w.qk8 else "splitkv_fp8_kernel"
     return "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
 
 
@@ -551,11 +552,11 @@ def measure_mla(idx: int, steps: int, warmup: int, copies: int, clock_probe: boo
             meta = num_parts                       # the kernels derive the schedule themselves
         k = caches[i % len(caches)]
         api.mla_decode_splitkv(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
-                               g.k_scale)
+                               g.k_scale, w.qk8)
         if ev is not None:
             ev[0].record(ev[1] + 2)
         api.mla_decode_combine(g.q, k, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal, meta, bufs,
-                               g.k_scale)
+                               g.k_scale, w.qk8)
         if ev is not None:
             ev[0].record(ev[1] + 3)
 
@@ -668,6 +669,7 @@ def cpu_leg(m: dict, seconds: float, check_all: bool = True):
     oracle on every request (`check_all`) or on the requests timed."""
     import numpy as np
     from oracle import dequantize_cache, oracle_decode_rows
+    from oracle.fp8 import quantize_q_rows
 
     try:
         from threadpoolctl import threadpool_info
@@ -677,7 +679,8 @@ def cpu_leg(m: dict, seconds: float, check_all: bool = True):
         threads = len(os.sched_getaffinity(0))
     host = m["host"]
     w = m["workload"]
-    qf = host.q.double().numpy()
+    # the fp8 query-key product computes with the quantized query rows
+    qf = quantize_q_rows(host.q) if w.qk8 else host.q.double().numpy()
     kf = dequantize_cache(host.k_cache, host.k_scale) if w.kv == "fp8" else host.k_cache.double().numpy()
     B, s_q, h_q, _ = qf.shape
     R = s_q * h_q
@@ -761,9 +764,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=None,
-                    help="one workload only, 1..12 (default: the five configurations 1-5, headline 2); 6, 11 "
-                         "and 12 are 3, 2 and 5 with an fp8 cache, 7-10 use the MHA path (7-9 GQA, 9 with fp8 "
-                         "K/V; 10 multi-query)")
+                    help="one workload only, 1..14 (default: the five configurations 1-5, headline 2); 6, 11 "
+                         "and 12 are 3, 2 and 5 with an fp8 cache, 13 and 14 are 11 and 12 with the fp8 "
+                         "query-key product, 7-10 use the MHA path (7-9 GQA, 9 with fp8 K/V; 10 multi-query)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the reference steps with a precomputed schedule (profiled runs: only the "

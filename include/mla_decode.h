@@ -97,7 +97,16 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
  * bits; here the latent cache itself is stored in fp8, converted exactly to
  * bf16 on chip, and the page scale is applied to the scores and to the
  * probabilities, which halves the bytes a memory-bound decode reads. */
-typedef enum { MLA_KV_SAME = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype;
+/* MLA_KV_FP8_E4M3_QK8: the same fp8 cache, and the query-key product in fp8
+ * as those pages describe it: each query row (one token of one head) is
+ * taken to e4m3 codes with its own power-of-two scale 2^k, the smallest with
+ * max|q| * 2^-k <= 448 (k = 0 for a row of zeros; the scaling is exact and
+ * the rounding to nearest e4m3, ties to even, the only one), and S = Q.K^T
+ * runs on the fp8 matrix instructions from the cached codes directly.  The
+ * softmax and the value product are those of MLA_KV_FP8_E4M3.  The result
+ * is the attention of the dequantized q over the dequantized cache; any
+ * s_q*h_q (the 64-row kernel runs every shape). */
+typedef enum { MLA_KV_SAME = 0, MLA_KV_FP8_E4M3 = 1, MLA_KV_FP8_E4M3_QK8 = 2 } mla_kv_dtype;
 
 /* Text of the last error raised on the calling thread ("" if none); never NULL.
  * The pointer stays valid until the next call into the library on this thread.

@@ -220,7 +220,7 @@ def workspace_size(batch: int, s_q: int, h_q: int, num_parts: int) -> int:
 
 
 def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
-                workspace, out, lse, k_scale=None, num_parts=None) -> DecodeArgs:
+                workspace, out, lse, k_scale=None, num_parts=None, qk_fp8=False) -> DecodeArgs:
     a = DecodeArgs()
     a.dtype = DTYPE_CODES[q.dtype]
     a.batch, a.s_q, a.h_q = q.shape[0], q.shape[1], q.shape[2]
@@ -245,7 +245,7 @@ def _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, s
     a.out = out.data_ptr()
     a.out_stride[:] = list(out.stride()[:3])
     a.lse = lse.data_ptr()
-    a.kv_dtype = 1 if k_cache.dtype == torch.float8_e4m3fn else 0
+    a.kv_dtype = (2 if qk_fp8 else 1) if k_cache.dtype == torch.float8_e4m3fn else 0
     a.k_scale = k_scale.data_ptr() if k_scale is not None else None
     return a
 
@@ -344,15 +344,21 @@ def _schedule(metadata, q, k_cache, cache_seqlens):
     return sched, offs, sched.shape[0]
 
 
+def _check_qk_fp8(k_cache, qk_fp8):
+    if qk_fp8 and k_cache.dtype != torch.float8_e4m3fn:
+        raise ValueError("qk_fp8 needs an fp8 (float8_e4m3fn) cache")
+
+
 def _call(fn_name, q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
-          k_scale=None):
+          k_scale=None, qk_fp8=False):
     _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale)
+    _check_qk_fp8(k_cache, qk_fp8)
     sched, offs, parts = _schedule(metadata, q, k_cache, cache_seqlens)
     if buffers is None:
         buffers = DecodeBuffers(q, parts)
     _check_outputs(q, buffers.out, buffers.lse, D_V)
     a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs,
-                    buffers.workspace, buffers.out, buffers.lse, k_scale, num_parts=parts)
+                    buffers.workspace, buffers.out, buffers.lse, k_scale, num_parts=parts, qk_fp8=qk_fp8)
     _check(getattr(lib(), fn_name)(ctypes.byref(a), _stream_ptr(q.device)))
     return buffers.out, buffers.lse
 
@@ -361,7 +367,7 @@ def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor
                cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
                metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
                buffers: Optional[DecodeBuffers] = None,
-               k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+               k_scale: Optional[torch.Tensor] = None, qk_fp8: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MLA decode.  Returns (out [B, s_q, h_q, 512] in q's dtype,
     lse [B, s_q, h_q] fp32, natural log).  `metadata` is get_metadata's result,
     or a partition count: the kernels then derive the same schedule from
@@ -370,48 +376,51 @@ def mla_decode(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor
     get_metadata beyond.  `buffers` lets a caller reuse outputs.  An
     fp8 cache (torch.float8_e4m3fn, with a bf16 q) takes an
     optional per-page fp32 scale `k_scale` [num_pages] (any finite value; the
-    cached row is code * scale)."""
+    cached row is code * scale).  qk_fp8 (fp8 cache only) also takes each
+    query row to e4m3 codes with a power-of-two scale and forms Q.K^T on the
+    fp8 matrix instructions (MLA_KV_FP8_E4M3_QK8)."""
     return _call("mla_decode", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
-                 k_scale)
+                 k_scale, qk_fp8)
 
 
 def mla_decode_fused(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
                      cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
                      metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
                      buffers: Optional[DecodeBuffers] = None,
-                     k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     k_scale: Optional[torch.Tensor] = None, qk_fp8: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged MLA decode with the merge of split requests (up to 4 pieces) done
     inside the split-KV kernel; same result as mla_decode.  `buffers` must come
     from DecodeBuffers (zero-filled workspace) and not be shared by two calls
     in flight on different streams."""
     return _call("mla_decode_fused", q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata,
-                 buffers, k_scale)
+                 buffers, k_scale, qk_fp8)
 
 
 def mla_decode_splitkv(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
-                       k_scale=None):
+                       k_scale=None, qk_fp8=False):
     """First phase only (the split-KV kernel)."""
     return _call("mla_decode_splitkv", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
-                 metadata, buffers, k_scale)
+                 metadata, buffers, k_scale, qk_fp8)
 
 
 def mla_decode_combine(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, metadata, buffers,
-                       k_scale=None):
+                       k_scale=None, qk_fp8=False):
     """Second phase only (merge of split pieces)."""
     return _call("mla_decode_combine", q, k_cache, block_table, cache_seqlens, softmax_scale, causal,
-                 metadata, buffers, k_scale)
+                 metadata, buffers, k_scale, qk_fp8)
 
 
 def mla_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
                        cache_seqlens: torch.Tensor, softmax_scale: float, causal: bool = False,
                        metadata: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       k_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                       k_scale: Optional[torch.Tensor] = None, qk_fp8: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """mla_decode with the library's static per-GPU workspace: no workspace
     tensor, and the C call allocates nothing (pass `out`/`lse` and `metadata`
     to keep this function from allocating them).  Calls that overlap in time
     on one GPU share that workspace and race."""
     _validate_tensors(q, k_cache, block_table, cache_seqlens, k_scale)
+    _check_qk_fp8(k_cache, qk_fp8)
     sched, offs, parts = _schedule(metadata, q, k_cache, cache_seqlens)
     B, s_q, h_q, _ = q.shape
     if out is None:
@@ -420,7 +429,7 @@ def mla_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, block_table: torc
         lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
     _check_outputs(q, out, lse, D_V)
     a = _build_args(q, k_cache, block_table, cache_seqlens, softmax_scale, causal, sched, offs, None, out, lse,
-                    k_scale, num_parts=parts)
+                    k_scale, num_parts=parts, qk_fp8=qk_fp8)
     _check(lib().mla_decode_noalloc(ctypes.byref(a), _stream_ptr(q.device)))
     return out, lse
 

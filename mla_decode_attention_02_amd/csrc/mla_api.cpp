@@ -110,9 +110,10 @@ mla_status check_decode(const mla_decode_args* a) {
     return fail(MLA_ERROR_UNSUPPORTED, "page_size must be 64 (got %d)", a->page_size);
   mla_status st = check_shape(a->batch, a->s_q, a->h_q, a->h_kv);
   if (st != MLA_SUCCESS) return st;
-  if (a->kv_dtype != MLA_KV_SAME && a->kv_dtype != MLA_KV_FP8_E4M3)
-    return fail(MLA_ERROR_UNSUPPORTED, "kv_dtype %d is not MLA_KV_SAME (0) or MLA_KV_FP8_E4M3 (1)", a->kv_dtype);
-  if (a->kv_dtype == MLA_KV_FP8_E4M3 && a->dtype != MLA_DTYPE_BF16)
+  if (a->kv_dtype != MLA_KV_SAME && a->kv_dtype != MLA_KV_FP8_E4M3 && a->kv_dtype != MLA_KV_FP8_E4M3_QK8)
+    return fail(MLA_ERROR_UNSUPPORTED,
+                "kv_dtype %d is not MLA_KV_SAME (0), MLA_KV_FP8_E4M3 (1) or MLA_KV_FP8_E4M3_QK8 (2)", a->kv_dtype);
+  if (a->kv_dtype != MLA_KV_SAME && a->dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERROR_UNSUPPORTED, "an fp8 cache needs dtype bf16");
   if (a->k_scale && !aligned(a->k_scale, 4)) return fail(MLA_ERROR_INVALID_VALUE, "k_scale must be 4-byte aligned");
   if (a->num_pages <= 0 || a->max_pages_per_seq <= 0 || a->num_parts <= 0)
@@ -123,7 +124,7 @@ mla_status check_decode(const mla_decode_args* a) {
     return fail(MLA_ERROR_INVALID_VALUE, "sched and split_offsets must both be given or both be NULL");
   if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->workspace, 16))
     return fail(MLA_ERROR_INVALID_VALUE, "q, out and workspace must be 16-byte aligned");
-  if (!aligned(a->k_cache, a->kv_dtype == MLA_KV_FP8_E4M3 ? 8 : 16))
+  if (!aligned(a->k_cache, a->kv_dtype != MLA_KV_SAME ? 8 : 16))
     return fail(MLA_ERROR_INVALID_VALUE, "k_cache must be 16-byte aligned (8 for an fp8 cache)");
   if (!aligned(a->lse, 4) || !aligned(a->block_table, 4) || !aligned(a->cache_seqlens, 4) ||
       !aligned(a->sched, 4) || !aligned(a->split_offsets, 4))
@@ -161,7 +162,8 @@ mla::DecodeParams make_params(const mla_decode_args* a) {
   p.q_s0 = a->q_stride[0]; p.q_s1 = a->q_stride[1]; p.q_s2 = a->q_stride[2];
   p.k = a->k_cache;
   p.k_s0 = a->k_stride[0]; p.k_s1 = a->k_stride[1];
-  p.kv_fp8 = a->kv_dtype == MLA_KV_FP8_E4M3;
+  p.kv_fp8 = a->kv_dtype != MLA_KV_SAME;
+  p.qk8 = a->kv_dtype == MLA_KV_FP8_E4M3_QK8;
   p.k_scale = a->k_scale;
   p.block_table = a->block_table;
   p.bt_s = a->bt_stride;
@@ -258,9 +260,12 @@ mla_status launch_splitkv(const mla_decode_args* args, const mla::DecodeParams& 
   const int tile = tile_rows(p.rows);
   const int m_blocks = (p.rows + tile - 1) / tile;
   hipStream_t hs = stream;
-  hipError_t e = tile == 16  ? mla::launch_splitkv_narrow(p, args->dtype, hs)
-                 : p.kv_fp8 ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
-                            : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
+  // the fp8 query-key product exists in the 64-row kernel only, which also
+  // takes up to 16 rows (one row tile, the rows past them masked)
+  hipError_t e = p.qk8        ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
+                 : tile == 16 ? mla::launch_splitkv_narrow(p, args->dtype, hs)
+                 : p.kv_fp8   ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
+                              : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
   if (e != hipSuccess) return hip_fail(e, "split-KV launch");
   return ok();
 }

@@ -58,6 +58,7 @@ struct DecodeParams {
   float* part_o;            // [slots, rows, 512] fp32
   float* part_lse;          // [slots, rows]
   int kv_fp8;               // k_cache holds fp8 e4m3 codes (else the dtype of q)
+  int qk8;                  // fp8 cache and fp8 query codes for the Q.K^T product
   const float* k_scale;     // fp8: per-page scale (K = code * scale), or null for 1
   int* counters;            // [m_blocks, batch] arrivals per row tile of a split request
   int* req_slots;           // [batch][2] first piece slot and piece count per request,

@@ -55,6 +55,75 @@ __device__ __forceinline__ void load_q_frag8(const DecodeParams& p, int b, int r
   }
 }
 
+// ---------------------------------------------------- fp8 query codes --
+// Q taken into fp8 for an fp8 query-key product (page "DeepSeek开源FlashMLA全解析：
+// 性能革命背后的技术密码", section "1.2 计算模式创新：混合精度矩阵乘法", and page
+// "云上AI推理新突破：FlashMLA赋能DeepSeek-V2-Lite提速16%", section "3. 动态精度缩放":
+// q and k in fp8 for Q.K^T, the softmax and P.V in 16 bits).  Each query row
+// has its own power-of-two scale 2^k, the smallest with max|q| * 2^-k <= 448
+// (the largest e4m3 value; k = 0 for a row of zeros), so the scaling is exact
+// and the e4m3 rounding (to nearest, ties to even) the only one.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Operand layout of the 16x16x128 fp8 MFMA as used here: within a lane group
+// g (lanes 16g .. 16g+15, one row each), step m covers columns
+// 128m + 32g .. +32, byte j of the lane's eight registers being column
+// 128m + 32g + j; the same for the Q and K operands (the unit pairs byte j of
+// a lane group in both).  Step 4 holds columns 512 .. 575 in groups 0 and 1
+// and zeros in groups 2 and 3.
+constexpr int kQ8Steps = 5;
+
+__device__ __forceinline__ int q8_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  (void)frexpf(amax, &e);                    // amax = f * 2^e, f in [0.5, 1)
+  int k = e - 9;                             // amax * 2^-k in [256, 512)
+  if (ldexpf(amax, -k) > 448.f) ++k;
+  return k;
+}
+
+// Codes of query row `row` for lane group g (zeros past the rows), and the
+// row's scale 2^k.  Two passes over the row (the maximum, then the codes):
+// holding the whole row's raw values between them would cost 80 registers.
+__device__ __forceinline__ void load_q_codes8(const DecodeParams& p, int b, int row, int g, i32x8 (&qc)[kQ8Steps],
+                                              float& qscale) {
+  const bool live = row < p.rows;
+  const int tok = live ? row / p.h_q : 0;
+  const int head = live ? row - tok * p.h_q : 0;
+  const __bf16* base = (const __bf16*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2 + 32 * g;
+  auto raw = [&](int m, int h) {
+    const bool in = live && (m < 4 || g < 2);
+    return in ? *(const u32x4*)(base + 128 * m + 8 * h) : u32x4{0, 0, 0, 0};
+  };
+  auto val = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xFFFF0000u) : (w << 16)); };
+  float amax = 0.f;
+#pragma unroll
+  for (int m = 0; m < kQ8Steps; ++m)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 w = raw(m, h);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) amax = fmaxf(amax, fmaxf(fabsf(val(w[d], 0)), fabsf(val(w[d], 1))));
+    }
+  amax = max_across_groups(amax);            // the four lane groups of the row
+  const int k = q8_exponent(amax);
+  qscale = ldexpf(1.f, k);
+#pragma unroll
+  for (int m = 0; m < kQ8Steps; ++m)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 w = raw(m, h);
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+        // dword 2h + d2 of the operand: columns 8h + 4 d2 .. +4
+        const uint32_t w0 = w[2 * d2], w1 = w[2 * d2 + 1];
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(val(w0, 0), -k), ldexpf(val(w0, 1), -k), 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(val(w1, 0), -k), ldexpf(val(w1, 1), -k), c, true);
+        qc[m][2 * h + d2] = c;
+      }
+    }
+}
+
 __device__ __forceinline__ u32x2 ld_lds_tr8(const MLA_LDS char* p) {
   typedef int v2i __attribute__((ext_vector_type(2)));
   const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS v2i*)p);

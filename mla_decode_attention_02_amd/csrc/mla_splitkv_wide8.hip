@@ -32,6 +32,11 @@ constexpr int kDmaW8 = 5;                       // cache pieces per score wave a
 constexpr int kHalfBuf8 = 4 * kDmaW8 * 1024;    // 20 KiB: the image and the tail of the padding pieces
 static_assert(kHalfBuf8 >= kHalf8 && kHalfSlots8 <= 4 * kDmaW8 * 64, "half-page pieces");
 
+// kQ8: the query rows are taken into fp8 too (load_q_codes8) and S^T = K.Q^T
+// runs on the 16x16x128 fp8 MFMA straight from the cached codes in LDS (five
+// steps of 128 columns, the last half zero); the probabilities and P.V are
+// the same as without it.
+template <bool kQ8>
 __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p) {
   typedef __bf16 T;
   __shared__ __attribute__((aligned(1024))) char hb0_raw[kHalfBuf8];
@@ -109,8 +114,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p
       bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
       const int nh = half_pages(c);
       const int qrow = mrow0 + srow;
-      u32x4 qf[18];
-      load_q_frag8(p, c.b, qrow, g, qf);
+      u32x4 qf[kQ8 ? 1 : 18];
+      i32x8 qc[kQ8 ? kQ8Steps : 1];
+      float qscale = 1.f;                       // 2^k of the row's fp8 codes
+      if constexpr (kQ8) load_q_codes8(p, c.b, qrow, g, qc, qscale);
+      else load_q_frag8(p, c.b, qrow, g, qf);
       const int cnt = qrow < p.rows ? visible_count(c.n, p.s_q, qrow / p.h_q, p.causal) : 0;
       float m_run = -INFINITY;   // running max of row srow, log2 units
       float l_part = 0.f;        // this lane's share of its running sum
@@ -159,26 +167,57 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p
         // S^T for keys li (tile 0) and 16 + li (tile 1) x 16 rows
         const MLA_LDS char* rp0 = kb + li * kRow8;
         const MLA_LDS char* rp1 = rp0 + 16 * kRow8;
-        u32x4 k0[9], k1[9];
-#pragma unroll
-        for (int m = 0; m < 9; ++m) k0[m] = ld_lds16(rp0 + (((4 * m + g) ^ krot) << 4));
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        static_for<0, 9>([&](auto mc) {
-          constexpr int m = decltype(mc)::value;
-          s0 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][0], k0[m][1]}), qf[2 * m], s0);
-          s0 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][2], k0[m][3]}), qf[2 * m + 1], s0);
-          k1[m] = ld_lds16(rp1 + (((4 * m + g) ^ krot ^ 2) << 4));
-          if constexpr (m <= kDmaW8) load(std::integral_constant<int, H + 2>{}, t + 2, hs, mc);
-        });
+        if constexpr (kQ8) {
+          // K operand of step m: chunks 8m + 2g and 8m + 2g + 1 of the key's
+          // row (one swizzled pair); zeros past the row (step 4, groups 2, 3)
+          auto kop = [&](const MLA_LDS char* rp, int rot, int m) {
+            const u32x4 lo = ld_lds16(rp + (((8 * m + 2 * g) ^ rot) << 4));
+            const u32x4 hi = ld_lds16(rp + (((8 * m + 2 * g + 1) ^ rot) << 4));
+            const bool in = m < 4 || g < 2;
+            return i32x8{in ? (int)lo[0] : 0, in ? (int)lo[1] : 0, in ? (int)lo[2] : 0, in ? (int)lo[3] : 0,
+                         in ? (int)hi[0] : 0, in ? (int)hi[1] : 0, in ? (int)hi[2] : 0, in ? (int)hi[3] : 0};
+          };
+          // both tiles' operands two steps ahead of their MFMAs (a ring of three)
+          i32x8 ka[3], kb1[3];
+          static_for<0, 2>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            ka[m] = kop(rp0, krot, m);
+            kb1[m] = kop(rp1, krot ^ 2, m);
+          });
+          static_for<0, kQ8Steps>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr (m + 2 < kQ8Steps) {
+              ka[(m + 2) % 3] = kop(rp0, krot, m + 2);
+              kb1[(m + 2) % 3] = kop(rp1, krot ^ 2, m + 2);
+            }
+            s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m % 3], qc[m], s0, 0, 0, 0, 127, 0, 127);
+            s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kb1[m % 3], qc[m], s1, 0, 0, 0, 127, 0, 127);
+            load(std::integral_constant<int, H + 2>{}, t + 2, hs, mc);            // pieces 0 .. 4
+            if constexpr (m == 0) load(std::integral_constant<int, H + 2>{}, t + 2, hs,
+                                       std::integral_constant<int, kDmaW8>{});    // the scale
+          });
+        } else {
+          u32x4 k0[9], k1[9];
 #pragma unroll
-        for (int m = 0; m < 9; ++m) {
-          s1 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k1[m][0], k1[m][1]}), qf[2 * m], s1);
-          s1 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k1[m][2], k1[m][3]}), qf[2 * m + 1], s1);
+          for (int m = 0; m < 9; ++m) k0[m] = ld_lds16(rp0 + (((4 * m + g) ^ krot) << 4));
+          static_for<0, 9>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            s0 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][0], k0[m][1]}), qf[2 * m], s0);
+            s0 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][2], k0[m][3]}), qf[2 * m + 1], s0);
+            k1[m] = ld_lds16(rp1 + (((4 * m + g) ^ krot ^ 2) << 4));
+            if constexpr (m <= kDmaW8) load(std::integral_constant<int, H + 2>{}, t + 2, hs, mc);
+          });
+#pragma unroll
+          for (int m = 0; m < 9; ++m) {
+            s1 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k1[m][0], k1[m][1]}), qf[2 * m], s1);
+            s1 = Dt<T>::mfma32(codes8_to_bf16(u32x2{k1[m][2], k1[m][3]}), qf[2 * m + 1], s1);
+          }
         }
         // online softmax of row srow over keys 4g+r (tile 0) and 16+4g+r (tile 1);
         // the scale multiplies before the maximum (it may be of either sign)
         const float ksc = scaled ? sbuf(Hc)[wave * 64] : 1.f;
-        const float sl = p.scale_log2 * ksc;
+        const float sl = p.scale_log2 * ksc * qscale;          // qscale: 2^k (exact), or 1
         float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
         const int key0 = (2 * c.lo + t) * kHalfRows + 4 * g;
         float mx = -INFINITY;
@@ -317,7 +356,8 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p
 }
 
 hipError_t launch_splitkv_wide_fp8(const DecodeParams& p, int m_blocks, hipStream_t st) {
-  hipLaunchKernelGGL(splitkv_wide_fp8_kernel, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
+  if (p.qk8) hipLaunchKernelGGL(splitkv_wide_fp8_kernel<true>, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
+  else hipLaunchKernelGGL(splitkv_wide_fp8_kernel<false>, dim3(p.num_parts, m_blocks), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ class Workload:
     seqlen_range: Optional[tuple] = None          # inclusive (lo, hi) uniform integers
     seed: int = 0
     kv: str = "same"                              # "same" (dtype) or "fp8" (e4m3 codes + page scales)
+    qk8: bool = False                             # fp8 cache and the fp8 query-key product
     description: str = field(default="", compare=False)
 
     @property
@@ -71,7 +72,8 @@ class Workload:
 
 # The workloads the measurements are quoted on.  Seeds are the index, except
 # for the fp8-cache variants 6, 11 and 12: workloads 3, 2 and 5 (same seed,
-# lengths and page table) with an fp8 cache.  (7..10 are the MHA workloads.)
+# lengths and page table) with an fp8 cache, and 13 and 14: workloads 11 and
+# 12 with the fp8 query-key product as well.  (7..10 are the MHA workloads.)
 WORKLOADS = {
     1: Workload("tiny", 2, 1, 16, "bf16", 1.0, False, seqlens=(64, 100), seed=1,
                 description="B2 s_q1 h_q16 bf16, s_k {64,100}, non-causal"),
@@ -94,6 +96,12 @@ WORKLOADS = {
     12: Workload("longctx_bs4_hq128_fp8kv", 4, 1, 128, "bf16", 1.0, False,
                  seqlens=(65536, 98304, 131072, 131072), seed=5, kv="fp8",
                  description="B4 s_q1 h_q128 bf16 q, fp8 e4m3 KV with per-page scales, s_k {64K,96K,128K,128K}"),
+    13: Workload("bs64_hq128_sk4096_fp8kv_qk8", 64, 1, 128, "bf16", 1.0, False, seqlens=(4096,) * 64, seed=2,
+                 kv="fp8", qk8=True,
+                 description="workload 11 with q taken into fp8 (per-row power-of-two scale) for an fp8 Q.K^T"),
+    14: Workload("longctx_bs4_hq128_fp8kv_qk8", 4, 1, 128, "bf16", 1.0, False,
+                 seqlens=(65536, 98304, 131072, 131072), seed=5, kv="fp8", qk8=True,
+                 description="workload 12 with q taken into fp8 (per-row power-of-two scale) for an fp8 Q.K^T"),
 }
 
 

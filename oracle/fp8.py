@@ -110,3 +110,67 @@ def dequantize_heads(codes, scale=None) -> np.ndarray:
     if s.shape != (v.shape[0], v.shape[2]):
         raise ValueError("scale must hold one value per page and KV head")
     return v * s[:, None, :, None]
+
+
+# ------------------------------------------------- fp8 query quantization --
+# [RUIBAO-FP8] and [LITE-FP8] also take the query into fp8 for the query-key
+# product.  Reading: each query row (one token of one head, its 576 values) is
+# quantized on its own: with a = max |q| over the row, the scale is the power
+# of two 2^k with the smallest k such that a * 2^-k <= 448 (the largest e4m3
+# value; k = 0 for a row of zeros), and each value becomes the e4m3 code
+# nearest to q * 2^-k, ties to the code with an even last mantissa bit.  The
+# scaling is exact, so the rounding to e4m3 is the only one.  The product is
+# then the attention of decode.py with q replaced by code value * 2^k.
+
+E4M3_MAX = 448.0
+_FINITE = np.array(sorted({abs(v) for v in _VALUES if not math.isnan(v)}), dtype=np.float64)   # 0 .. 448
+_FINITE_CODE = np.array([next(c for c in range(128) if _VALUES[c] == v) for v in _FINITE], dtype=np.uint8)
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Nearest e4m3fn code to each float with |x| <= 448 (ties to the even
+    code); uint8 array of x's shape.  A value that rounds to zero keeps its
+    sign in the code (0x80 for negative values)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any() or (np.abs(x) > E4M3_MAX).any():
+        raise ValueError("values must be finite and within +-448")
+    a = np.abs(x)
+    hi = np.searchsorted(_FINITE, a, side="left")          # first representable >= a
+    lo = np.maximum(hi - 1, 0)
+    hi = np.minimum(hi, len(_FINITE) - 1)
+    dlo, dhi = a - _FINITE[lo], _FINITE[hi] - a
+    c_lo, c_hi = _FINITE_CODE[lo], _FINITE_CODE[hi]
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (c_hi % 2 == 0) & (c_lo % 2 == 1))
+    code = np.where(take_hi, c_hi, c_lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def row_scale_exponent(a: float) -> int:
+    """The k of the query row scale 2^k for a row maximum a >= 0 (see above)."""
+    if a == 0.0:
+        return 0
+    _, e = math.frexp(a)                   # a = f * 2^e, f in [0.5, 1)
+    k = e - 9                              # a * 2^-k in [256, 512)
+    if math.ldexp(a, -k) > E4M3_MAX:
+        k += 1
+    assert math.ldexp(a, -k) <= E4M3_MAX < math.ldexp(a, -(k - 1))
+    return k
+
+
+def quantize_q_rows(q) -> np.ndarray:
+    """q [..., 576] (bf16/fp16 tensor or array) -> the float64 values the fp8
+    query-key product uses: code value * 2^k, one k per row."""
+    try:
+        import torch
+
+        if isinstance(q, torch.Tensor):
+            q = q.detach().cpu().double().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    q = np.asarray(q, dtype=np.float64)
+    rows = q.reshape(-1, q.shape[-1])
+    out = np.empty_like(rows)
+    for i, r in enumerate(rows):
+        k = row_scale_exponent(float(np.abs(r).max()) if r.size else 0.0)
+        out[i] = decode_e4m3fn(encode_e4m3fn(np.ldexp(r, -k))) * math.ldexp(1.0, k)
+    return out.reshape(q.shape)

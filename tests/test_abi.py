@@ -166,8 +166,10 @@ BREAKS = [
     ("scale neg", lambda a: setattr(a, "softmax_scale", -0.5), INVALID),
     ("causal", lambda a: setattr(a, "causal", 2), INVALID),
     ("workspace small", lambda a: setattr(a, "workspace_bytes", 1024), WS_SMALL),
-    ("kv_dtype", lambda a: setattr(a, "kv_dtype", 2), UNSUPPORTED),
+    ("kv_dtype", lambda a: setattr(a, "kv_dtype", 3), UNSUPPORTED),
     ("fp8 with fp16 q", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "dtype", 1)), UNSUPPORTED),
+    ("fp8 Q.K with fp16 q", lambda a: (setattr(a, "kv_dtype", 2), setattr(a, "dtype", 1)), UNSUPPORTED),
+    ("fp8 Q.K k misaligned", lambda a: (setattr(a, "kv_dtype", 2), setattr(a, "k_cache", (1 << 21) + 4)), INVALID),
     ("fp8 k misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "k_cache", (1 << 21) + 4)), INVALID),
     ("k_scale misaligned", lambda a: (setattr(a, "kv_dtype", 1), setattr(a, "k_scale", 10 * (1 << 20) + 2)),
      INVALID),

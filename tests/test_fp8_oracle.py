@@ -131,3 +131,79 @@ def test_fp8_cache_brute_force():
 def test_generator_rejects_fp8_with_fp16():
     with pytest.raises(ValueError):
         make_inputs(1, 1, 1, "fp16", seqlens=(3,), kv_dtype="fp8")
+
+
+# ---------------------------------------------- fp8 query quantization --
+from oracle.fp8 import encode_e4m3fn, quantize_q_rows, row_scale_exponent  # noqa: E402
+
+
+def test_encoder_inverts_the_decoder_on_every_code():
+    codes = np.array([c for c in range(256) if not math.isnan(e4m3fn_value(c))], dtype=np.uint8)
+    v = decode_e4m3fn(codes)
+    back = encode_e4m3fn(v)
+    assert np.array_equal(decode_e4m3fn(back), v)
+    nz = v != 0                                # zeros may come back as either sign
+    assert np.array_equal(back[nz], codes[nz])
+
+
+def test_encoder_matches_torch_on_every_bf16_value_in_range():
+    # torch's float8_e4m3fn cast rounds to nearest, ties to even: an
+    # independent implementation of the same rounding
+    x = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()
+    x = x[torch.isfinite(x) & (x.abs() <= 448)]
+    ref = x.to(torch.float8_e4m3fn).float().double().numpy()
+    assert np.array_equal(decode_e4m3fn(encode_e4m3fn(x.double().numpy())), ref)
+
+
+@pytest.mark.parametrize("x,value", [
+    (1.0625, 1.0),        # halfway between 1 and 1.125: the even code (1.0)
+    (1.1875, 1.25),       # halfway between 1.125 and 1.25: the even code (1.25)
+    (-1.0625, -1.0),
+    (448.0, 448.0), (-448.0, -448.0),
+    (2.0 ** -10, 0.0),    # half the smallest subnormal: ties to zero (even)
+    (1.5 * 2.0 ** -10, 2.0 ** -9),
+    (3 * 2.0 ** -10, 2.0 ** -8),   # halfway between subnormals 1 and 2 (x 2^-9): the even one
+    (0.0, 0.0),
+])
+def test_encoder_ties_and_ends(x, value):
+    assert decode_e4m3fn(encode_e4m3fn(np.array([x])))[0] == value
+
+
+def test_encoder_rejects_values_beyond_the_range():
+    with pytest.raises(ValueError):
+        encode_e4m3fn(np.array([448.5]))
+
+
+@pytest.mark.parametrize("a,k", [(448.0, 0), (449.0, 1), (1.0, -8), (0.0, 0), (1.75, -8), (1.76, -7),
+                                 (2.0 ** -130, -138), (3.0e38, 120)])
+def test_row_scale_exponent(a, k):
+    # the smallest k with a * 2^-k <= 448
+    assert row_scale_exponent(a) == k
+    if a > 0:
+        assert math.ldexp(a, -k) <= 448.0 < math.ldexp(a, -(k - 1))
+
+
+def test_quantized_rows():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((3, 2, 4, 576)) * np.array([1e-3, 1.0, 50.0, 1e4])[None, None, :, None]
+    q[0, 0, 0] = 0.0                                      # a zero row stays zero
+    deq = quantize_q_rows(q)
+    assert not deq[0, 0, 0].any()
+    for idx in np.ndindex(q.shape[:-1]):
+        r, d = q[idx], deq[idx]
+        if not r.any():
+            continue
+        k = row_scale_exponent(float(np.abs(r).max()))
+        codes = d / math.ldexp(1.0, k)
+        # every value is an e4m3 value at the row's scale, within e4m3's
+        # rounding (half an ulp: 2^-4 relative for normals, 2^-10 absolute
+        # below 2^-6) of the original
+        assert np.array_equal(decode_e4m3fn(encode_e4m3fn(codes)), codes)
+        y = np.ldexp(r, -k)
+        assert np.all(np.abs(codes - y) <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10))
+        assert np.abs(codes).max() <= 448.0 and np.abs(codes).max() > 224.0 - 16.0   # the scale uses the range
+    # a row already on the e4m3 grid of its scale is unchanged
+    g = decode_e4m3fn(np.arange(0, 126, dtype=np.uint8))[:64] * 8.0
+    row = np.concatenate([g, np.zeros(512)])
+    row[5] = 448.0 * 8.0
+    assert np.array_equal(quantize_q_rows(row[None]), row[None])

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from oracle import dequantize_cache, oracle_decode, oracle_decode_rows, oracle_metadata
+from oracle.fp8 import quantize_q_rows
 from mla_decode_attention_02_amd import api
 from mla_decode_attention_02_amd.workloads import WORKLOADS, make_inputs, workload_inputs, workload_seqlens
 
@@ -41,12 +42,12 @@ def _gpu():
 ENTRIES = ["mla_decode", "mla_decode_fused"]
 
 
-def run(x, num_parts=None, entry="mla_decode", buffers=None):
+def run(x, num_parts=None, entry="mla_decode", buffers=None, qk_fp8=False):
     dev = torch.device("cuda:0")
     g = x.to(dev)
     meta = api.get_metadata(g.cache_seqlens, g.q.shape[1], g.q.shape[2], num_parts=num_parts)
     out, lse = getattr(api, entry)(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale,
-                                   g.causal, metadata=meta, buffers=buffers, k_scale=g.k_scale)
+                                   g.causal, metadata=meta, buffers=buffers, k_scale=g.k_scale, qk_fp8=qk_fp8)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), [m.cpu().numpy() for m in meta]
 
@@ -287,6 +288,96 @@ def test_fp8_unused_slots_and_pages_are_never_read_bitwise(h_q):
             x.k_scale[page] = float("nan")
     out2, lse2, _ = run(x, 4)
     assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+# ------------------------------------------------- fp8 query-key product --
+# The query rows are taken into e4m3 with a power-of-two scale per row
+# (MLA_KV_FP8_E4M3_QK8); the oracle applies the same quantization
+# (quantize_q_rows, pinned on the CPU) and runs the fp64 attention over the
+# quantized q and the dequantized cache, so the bar is the one of the other
+# paths: the kernel's fp8 products are exact in fp32.
+def qk8_reference(x, causal):
+    return oracle_decode(quantize_q_rows(x.q), kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("s_q,h_q,seqlens,causal,mode,parts", FP8_EDGE,
+                         ids=[f"sq{c[0]}_hq{c[1]}_{'c' if c[3] else 'n'}_{c[4]}_p{c[5]}" for c in FP8_EDGE])
+def test_qk8_small_parity(s_q, h_q, seqlens, causal, mode, parts, entry):
+    tag = f"fp8 Q.K {entry} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} scale={mode} parts={parts}"
+    _say(tag)
+    x = make_inputs(len(seqlens), s_q, h_q, "bf16", seqlens=seqlens, causal=causal, seed=sum(seqlens) + 11 * h_q,
+                    poison=True, extra_pages=2, kv_dtype="fp8", scale_mode=mode)
+    out, lse, _ = run(x, parts, entry, qk_fp8=True)
+    ref_o, ref_l = qk8_reference(x, causal)
+    compare(out, lse, ref_o, ref_l, tag)
+
+
+def test_qk8_differs_from_the_bf16_query_product():
+    # the fp8 rounding of q is visible: the bf16-q oracle is not what the
+    # kernel computes, the quantized-q oracle is
+    _say("fp8 Q.K: q rounding visible")
+    x = make_inputs(2, 1, 128, "bf16", seqlens=(700, 129), seed=91, kv_dtype="fp8")
+    out, lse, _ = run(x, 5, qk_fp8=True)
+    ref_o, ref_l = qk8_reference(x, False)
+    plain_o, plain_l = oracle_decode(x.q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, False)
+    compare(out, lse, ref_o, ref_l, "fp8 Q.K")
+    assert np.abs(lse - plain_l).max() > 4 * np.abs(lse - ref_l).max()
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_qk8_negative_zero_and_large_scales(h_q):
+    _say(f"fp8 Q.K: page scales, h_q={h_q}")
+    x = make_inputs(3, 1, h_q, "bf16", seqlens=(300, 129, 64), seed=92, kv_dtype="fp8")
+    x.k_scale[int(x.block_table[0, 1])] *= -1.5
+    x.k_scale[int(x.block_table[1, 0])] = 0.0
+    x.k_scale[int(x.block_table[2, 0])] *= 3.0
+    x.q[0, 0, 0] = 0.0                                   # one all-zero query row
+    out, lse, _ = run(x, 4, qk_fp8=True)
+    ref_o, ref_l = qk8_reference(x, False)
+    compare(out, lse, ref_o, ref_l, "fp8 Q.K page scales", tol_o=range_tol(ref_o))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_qk8_unused_slots_and_pages_are_never_read_bitwise(h_q):
+    _say(f"fp8 Q.K: NaN codes in unused slots and pages, h_q={h_q}")
+    seqlens = (70, 130, 3)
+    x = make_inputs(3, 1, h_q, "bf16", seqlens=seqlens, seed=93, extra_pages=4, kv_dtype="fp8")
+    out1, lse1, _ = run(x, 4, qk_fp8=True)
+    raw = x.k_cache.view(torch.uint8)
+    for b, nlen in enumerate(seqlens):
+        p = (nlen + 63) // 64
+        raw[int(x.block_table[b, p - 1]), nlen % 64:, 0, :] = 0x7F
+    used = set(int(v) for v in x.block_table.flatten().tolist() if v >= 0)
+    for page in range(x.k_cache.shape[0]):
+        if page not in used:
+            raw[page] = 0x7F
+            x.k_scale[page] = float("nan")
+    out2, lse2, _ = run(x, 4, qk_fp8=True)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_qk8_full_size_every_request():
+    # the headline shape with an fp8 cache and the fp8 query-key product
+    w = WORKLOADS[11]
+    _say(f"fp8 Q.K full size: {w.name}")
+    host = workload_inputs(11)
+    g = host.to(torch.device("cuda:0"))
+    out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal,
+                              k_scale=g.k_scale, qk_fp8=True)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    qd = quantize_q_rows(host.q)
+    kv = dequantize_cache(host.k_cache, host.k_scale)
+    num = den = 0.0
+    for b in range(w.batch):
+        o, l = oracle_decode_rows(qd, kv, host.block_table, host.cache_seqlens, host.softmax_scale, host.causal, b)
+        o = o.reshape(out[b].shape)
+        l = l.reshape(lse[b].shape)
+        assert np.abs(out[b] - o).max() <= TOL_O and np.abs(lse[b] - l).max() <= TOL_LSE, f"request {b}"
+        num += float(((out[b] - o) ** 2).sum())
+        den += float((o ** 2).sum())
+    assert math.sqrt(num / den) <= 1e-2
 
 
 # ------------------------------------------------------------ invariants --

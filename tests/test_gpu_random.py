@@ -108,6 +108,30 @@ def test_fp8_wide_random(seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
+def test_qk8_random(seed):
+    """The fp8 query-key product (q rows into e4m3 with a power-of-two scale)
+    on random shapes, any number of query rows, against the oracle over the
+    quantized q."""
+    from oracle.fp8 import quantize_q_rows
+
+    rng = np.random.default_rng(2700 + seed)
+    B, s_q, h_q, seqlens, causal, parts = _case(rng, 160)
+    mode = ["amax", "pow2", "none"][int(rng.integers(0, 3))]
+    tag = f"fp8 Q.K seed={seed} B={B} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {mode} parts={parts}"
+    _say(tag)
+    x = make_inputs(B, s_q, h_q, "bf16", seqlens=seqlens, causal=causal, seed=seed, poison=True, extra_pages=1,
+                    kv_dtype="fp8", scale_mode=mode)
+    g = x.to(torch.device("cuda:0"))
+    meta = parts if seed % 2 else api.get_metadata(g.cache_seqlens, s_q, h_q, num_parts=parts)
+    out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale, causal, metadata=meta,
+                              k_scale=g.k_scale, qk_fp8=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(quantize_q_rows(x.q), dequantize_cache(x.k_cache, x.k_scale), x.block_table,
+                                 x.cache_seqlens, x.softmax_scale, causal)
+    _compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag)
+
+
+@pytest.mark.parametrize("seed", range(12))
 def test_mha_random(seed):
     rng = np.random.default_rng(3000 + seed)
     B, s_q, _, seqlens, causal, parts = _case(rng, 8)
