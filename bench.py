@@ -45,7 +45,18 @@ import time
 METRIC = "MLA decode TFLOP/s + effective HBM GB/s (bs64,h_q128,s_k4096) & roofline %"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E datasheet peak
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 D_K, D_V, PAGE = 576, 512, 64
+
+
+def mla_mfma_peak(qk8: bool) -> float:
+    """MFMA peak for one MLA decode's contractions.  With the fp8 query-key
+    product the score FLOPs (576 of every 1088 per row and key) run at the fp8
+    rate and P.V at the bf16 one; the peak is the rate that finishes both
+    shares in the least time, 1088 / (576/5000 + 512/2500) = 3400 TFLOP/s."""
+    if not qk8:
+        return MFMA_PEAK_TFLOPS
+    return (D_K + D_V) / (D_K / MFMA_FP8_PEAK_TFLOPS + D_V / MFMA_PEAK_TFLOPS)
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -115,7 +126,9 @@ def _counter_rows(path):
 
 
 MFMA_PASS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
-             "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"]
+             "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_INSTS_MFMA",
+             "GRBM_GUI_ACTIVE"]
+MOPS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F8"]
 LDS_PASS = ["SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH",
             "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_LDS_DATA_FIFO_FULL", "GRBM_GUI_ACTIVE"]
 
@@ -147,9 +160,11 @@ def pipe_counters(out_dir: str, tag: str, kernel: str):
     l, nl, _ = sums(dirs["l"])
     clk_m = m["GRBM_GUI_ACTIVE"] / n_xcc
     clk_l = l["GRBM_GUI_ACTIVE"] / n_xcc
-    flops = 512.0 * (m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + m["SQ_INSTS_VALU_MFMA_MOPS_F16"])
+    mops = [c for c in MOPS if c in m]       # passes taken before the fp8 counter was added lack it
+    flops = 512.0 * sum(m[c] for c in mops)
     sclk = clk_m / (ns_m * 1e-9) / 1e6
     rec = {
+        "mfma_pass": [c for c in MFMA_PASS if c in m],
         "dispatches": [nm, nl],
         "sclk_mhz": round(sclk),
         "mfma_busy_frac": round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (clk_m * n_simd), 4),
@@ -166,7 +181,8 @@ def pipe_counters(out_dir: str, tag: str, kernel: str):
     lines = ["", "MFMA pipe and LDS (two further counter passes; sums over the dispatches counted):", "",
              f"- clock: GRBM_GUI_ACTIVE / {n_xcc} XCDs over the dispatch time = {rec['sclk_mhz']} MHz",
              f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x {n_simd} SIMDs) = {rec['mfma_busy_frac']:.3f}",
-             f"- MFMA work: SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F16 = {rec['mfma_tflops_per_dispatch'] * 1e3:.2f} GFLOP "
+             f"- MFMA work: {' + '.join(c[len('SQ_INSTS_VALU_MFMA_'):] for c in mops)} = "
+             f"{rec['mfma_tflops_per_dispatch'] * 1e3:.2f} GFLOP "
              f"per dispatch, {rec['mfma_tflops_s']:.0f} TFLOP/s over the dispatch time",
              f"- CU busy: SQ_BUSY_CU_CYCLES / (clock cycles x {n_cu} CUs) = {rec['cu_busy_frac']:.3f}",
              f"- waves waiting: SQ_WAIT_ANY / SQ_WAVE_CYCLES = {rec['wave_wait_frac']:.3f}",
@@ -225,6 +241,8 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
            "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4),
            "hbm_bytes_per_launch": int(hbm), "algorithmic_bytes_per_launch": int(alg),
            "dispatches_counted": [n_f, n_w]}
+    pipe = pipe_counters(out_dir, tag, kernel)
+    mfma_pass = pipe[0]["mfma_pass"] if pipe is not None else MFMA_PASS
     lines = [f"# {kernel} on {w.name} ({w.description})", "",
              "Commands (from the repository root on one MI355X, TMPDIR=/tmp):", "",
              "```",
@@ -238,7 +256,7 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
              f"python3 bench.py --calibrate-copy {COPY_MIB}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw_copy -o p -- "
              f"python3 bench.py --calibrate-copy {COPY_MIB}",
-             f"rocprofv3 --pmc {' '.join(MFMA_PASS)} --output-format csv -d gpurun_out/pmcm_{tag} -o p -- "
+             f"rocprofv3 --pmc {' '.join(mfma_pass)} --output-format csv -d gpurun_out/pmcm_{tag} -o p -- "
              f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
              f"rocprofv3 --pmc {' '.join(LDS_PASS)} --output-format csv -d gpurun_out/pmcl_{tag} -o p -- "
              f"python3 bench.py --workload {workload} --steps 6 --warmup 2 --no-cpu-baseline{ref}",
@@ -258,7 +276,6 @@ def summarize_profiles(out_dir: str, workload: int) -> str:
               f"- WRITE_SIZE {write_kib:.1f} KiB x {scale_w:.3f} = {write_kib * scale_w / 1024:.1f} MiB written",
               f"- HBM traffic {hbm / 1e6:.1f} MB per launch against {alg / 1e6:.1f} MB algorithmic "
               f"(ratio {hbm / alg:.2f})"]
-    pipe = pipe_counters(out_dir, tag, kernel)
     if pipe is not None:
         rec["pipe"] = pipe[0]
         lines += pipe[1]
@@ -629,7 +646,8 @@ def mla_record(idx: int, m: dict, warm: dict) -> dict:
                                                      kv_elem=1 if w.kv == "fp8" else 2)
     step_bytes = kv + qb + ob + lseb + tb
     kv_bytes = kv + qb + tb
-    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    peak = mla_mfma_peak(w.qk8)
+    ridge = peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
     bound = "hbm" if flops / step_bytes < ridge else "mfma"
     st, sk = _quantiles(m["step_ms"]), _quantiles(m["splitkv_ms"])
     ms_step = m["region_ms"] / m["steps"]
@@ -653,7 +671,8 @@ def mla_record(idx: int, m: dict, warm: dict) -> dict:
         "step_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "splitkv_tflops": round(flops / kv_med_s / 1e12, 2),
         "splitkv_gbps": round(kv_bytes / kv_med_s / 1e9, 1),
-        "splitkv_mfma_frac": round(flops / kv_med_s / 1e12 / MFMA_PEAK_TFLOPS, 4),
+        "splitkv_mfma_frac": round(flops / kv_med_s / 1e12 / peak, 4),
+        "mfma_peak_tflops": round(peak, 1),
         "splitkv_hbm_frac": round(kv_bytes / kv_med_s / 1e9 / HBM_PEAK_GBPS, 4),
         "kernel": mla_kernel_name(w),
         "algorithmic_bytes_splitkv": kv_bytes, "algorithmic_flops": flops,
@@ -747,8 +766,9 @@ def headline_roofline(rec: dict) -> dict:
                 "frac": round(ach / HBM_PEAK_GBPS, 4)}
     else:
         ach = flops / t / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+        peak = rec["mfma_peak_tflops"]
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
     roof["traffic"] = stored_traffic(rec["kernel"], rec["workload"])
     roof["kernel"] = rec["kernel"]
     roof["kernel_median_us"] = rec["splitkv_us"]["median"]
@@ -851,8 +871,9 @@ def main() -> int:
                    "kv_cache": "fp8_e4m3 + per-page fp32 scale" if w.kv == "fp8" else w.dtype},
         "effective_hbm_gbps": rec["step_gbps"],
         "effective_hbm_frac": round(rec["step_gbps"] / HBM_PEAK_GBPS, 4),
-        "mfma_frac": round(rec["step_tflops"] / MFMA_PEAK_TFLOPS, 4),
+        "mfma_frac": round(rec["step_tflops"] / rec["mfma_peak_tflops"], 4),
         "peaks": {"hbm_gbps": HBM_PEAK_GBPS, "mfma_tflops_bf16_fp16_dense": MFMA_PEAK_TFLOPS,
+                  "mfma_tflops_fp8_dense": MFMA_FP8_PEAK_TFLOPS, "mfma_tflops_this_path": rec["mfma_peak_tflops"],
                   "sclk_mhz_observed": rec.get("sclk_mhz_observed"), "sclk_mhz_peak": 2400},
         "roofline": headline_roofline(rec),
         "step_us": rec["step_us"],

@@ -105,3 +105,14 @@ def test_mla_record_rates_use_the_timed_step_count():
     flops = bench.algorithmic_counts(workload_seqlens(2), w.batch, w.s_q, w.h_q)[0]
     assert abs(rec["step_tflops"] - flops / 1e-4 / 1e12) < 0.01
     assert rec["splitkv_us"]["median"] == 90.0 and rec["metadata_us_median"] is None
+
+
+def test_fp8_query_key_path_is_priced_at_the_blended_mfma_peak():
+    # Q.K^T (576 of 1088 FLOPs per row and key) at the fp8 rate, P.V at the
+    # bf16 rate: the time at peak is the sum of the two shares' times
+    assert bench.mla_mfma_peak(False) == bench.MFMA_PEAK_TFLOPS
+    peak = bench.mla_mfma_peak(True)
+    assert abs(peak - 3400.0) < 1e-9
+    t = 576 / bench.MFMA_FP8_PEAK_TFLOPS + 512 / bench.MFMA_PEAK_TFLOPS
+    assert abs(1088 / t - peak) < 1e-9
+    assert bench.MFMA_PEAK_TFLOPS < peak < bench.MFMA_FP8_PEAK_TFLOPS
