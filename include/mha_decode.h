@@ -69,8 +69,9 @@ mla_status mha_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
  * Build the split-KV schedule of the batch*h_kv units on the device (one
  * small kernel): unit u has length cache_seqlens[u / h_kv] and is cut by the
  * rule of mla_get_metadata (cost ceil(n / 64) + MLA_FIXED_OVERHEAD per nonempty unit, costs
- * laid end to end in unit order, partition k takes the positions in
- * [k*W, (k+1)*W), W = ceil(total / num_parts)).  sched rows and split_offsets
+ * laid end to end in unit order with the overhead split around each unit's
+ * pages, partition k takes the positions in [k*W, (k+1)*W),
+ * W = ceil(total / num_parts)).  sched rows and split_offsets
  * [batch*h_kv + 1] have the format of mla_get_metadata, with units in place of
  * requests.  Errors: INVALID_VALUE, HIP.
  */

@@ -140,11 +140,12 @@ mla_status mla_get_metadata_shape(int num_cus, int batch, int s_q, int h_q, int 
  * Build the split-KV tile schedule on the device (one small kernel).
  * A nonempty request b costs c_b = P_b + F, P_b = ceil(cache_seqlens[b] / 64),
  * F = MLA_FIXED_OVERHEAD; empty requests cost 0.  Costs are laid end to end in
- * request order, request b starting at C_b with its F overhead units first, so
- * page p of request b sits at position C_b + F + p.  With T = sum of costs and
+ * request order, request b starting at C_b with F0 = floor(F / 2) overhead
+ * units, then its pages, then the other F - F0 units, so page p of request b
+ * sits at position C_b + F0 + p.  With T = sum of costs and
  * W = ceil(T / num_parts), partition k takes the pages whose positions fall in
  * [k*W, (k+1)*W).  Each partition then costs at most W + F, the page's quota
- * ceil(total / num_parts) + fixed overhead.
+ * ceil(total / num_parts) + fixed overhead, counting F for every piece.
  *   cache_seqlens  device int32 [batch], each >= 0, with
  *                  sum_b (P_b + F) < 2^31.
  *   num_parts      >= 1 (normally from mla_get_metadata_shape).

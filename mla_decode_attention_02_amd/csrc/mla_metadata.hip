@@ -5,12 +5,14 @@
 // request costs.
 //
 // Assignment rule: a nonempty request b costs c_b = pages_b + F.  The costs are
-// laid end to end in request order, request b starting at C_b with its F
-// overhead units first, so page p of request b sits at position C_b + F + p.
-// With T = sum of costs and W = ceil(T / num_parts), partition k takes the pages
-// whose positions fall in [k W, (k+1) W).  A partition pays at most one F that
-// lies outside its interval (a piece starting inside a request), so its cost
-// stays within the quota W + F.
+// laid end to end in request order, request b starting at C_b with
+// F0 = floor(F / 2) overhead units, then its pages, then the other F - F0, so
+// page p of request b sits at position C_b + F0 + p.  With T = sum of costs and
+// W = ceil(T / num_parts), partition k takes the pages whose positions fall in
+// [k W, (k+1) W).  Every piece costs F, but a partition's interval misses at
+// most F0 of its first piece's overhead and F - F0 of its last one's, so its
+// cost stays within the quota W + F; overhead on both sides of the pages makes
+// a request cut in two split in the middle.
 //
 // The rule itself lives in mla_sched.hpp as wave-level functions, which the
 // split-KV and combine kernels also evaluate in place when a call brings no

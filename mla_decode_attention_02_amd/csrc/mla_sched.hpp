@@ -5,8 +5,15 @@
 //
 // The rule is the one metadata_kernel applies: a nonempty unit u (a request)
 // costs c_u = pages_u + F, the costs lie end to end in unit order with unit u
-// starting at C_u and its F overhead positions first, and with T = sum c_u and
-// W = ceil(T / num_parts) partition k owns the page positions in [kW, (k+1)W).
+// starting at C_u, F0 = floor(F / 2) of its overhead positions ahead of its
+// pages and F - F0 after them, and with T = sum c_u and W = ceil(T / num_parts)
+// partition k owns the page positions in [kW, (k+1)W).  (A piece cut off at
+// either end of a partition then misses at most half of its F on the line, so
+// a cut request is split evenly.)
+//
+// The code below keeps the coordinates of the line with all F positions ahead
+// of a unit's pages (page p of unit u at C_u + F + p); there a page lies F - F0
+// further right, so partition k owns [kW + F - F0, (k+1)W + F - F0).
 // Every wave that needs a partition's row, or a unit's piece slots, derives it
 // from the lengths alone, so the kernels can run without the separate metadata
 // launch; the results are the integers metadata_kernel writes.
@@ -34,10 +41,11 @@ __device__ __forceinline__ int div_floor(int a, int w, double rw) {
 }
 
 // Partitions that the pages of a unit starting at `start` with cost `cost`
-// touch (0 for an empty unit).
+// touch (0 for an empty unit); its pages lie at start + F0 + p.
 __device__ __forceinline__ int sched_pieces(int start, int cost, int F, int width, double rw) {
   const int pages = cost > 0 ? cost - F : 0;
-  return pages > 0 ? div_floor(start + F + pages - 1, width, rw) - div_floor(start + F, width, rw) + 1 : 0;
+  const int first = start + (F >> 1);
+  return pages > 0 ? div_floor(first + pages - 1, width, rw) - div_floor(first, width, rw) + 1 : 0;
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave (all lanes active): a
@@ -119,7 +127,8 @@ __device__ __forceinline__ SchedRow sched_row(const int32_t* seqlens, int units,
   const int width = total > 0 ? (total + parts - 1) / parts : 1;
   const double rw = 1.0 / width;
   r.width = width;
-  const long long s = (long long)k * width;
+  // partition k in the all-ahead coordinates (the page positions shifted by F - F0)
+  const long long s = (long long)k * width + (F - (F >> 1));
   if (s >= total) return r;
   const int e = (int)min((long long)total, s + width);
   const int s32 = (int)s;
@@ -170,7 +179,7 @@ __device__ __forceinline__ SchedRow sched_row(const int32_t* seqlens, int units,
   }
   r.b1 = b1;
   r.p1 = last - cb1 - F + 1;
-  r.split0 = k - (c_s + F) / width;
+  r.split0 = k - (c_s + (F >> 1)) / width;  // partitions ahead of b0's first page
   r.slot0 = slot;
   return r;
 }

@@ -15,11 +15,18 @@ The pages give the quota and the goal, not the assignment rule.  Reading used
 here (listed in the design notes): every nonempty request b costs c_b = P_b + F
 (P_b = ceil(n_b / 64) pages, F = fixed overhead), empty requests cost 0.  The
 costs are laid end to end on one line in request order, request b occupying
-[C_b, C_b + c_b) with its F overhead units first and then one unit per page, so
-page p of request b sits at position C_b + F + p.  With T = sum of the costs and
-Q' = ceil(T / num_parts), partition k takes every page whose position lies in
-[k Q', (k+1) Q').  A partition pays one extra F at most (for a piece that starts
-inside a request), so its cost never exceeds the quota Q' + F.
+[C_b, C_b + c_b): F0 = floor(F / 2) overhead units, one unit per page, then the
+other F - F0 overhead units, so page p of request b sits at position
+C_b + F0 + p.  With T = sum of the costs and Q' = ceil(T / num_parts),
+partition k takes every page whose position lies in [k Q', (k+1) Q').
+
+Every piece pays F in the kernel, but the line holds F once per request: a
+piece that begins or ends at a cut gets only part of its F from the line.
+With the overhead on both sides of a request's pages, the two pieces at a cut
+lack F - F0 and F0 respectively instead of 0 and F, so a request cut in two
+is cut in the middle (e.g. 64 pages with F = 2: 32 + 32 rather than 31 + 33).
+A partition lacks at most F0 at its first piece and F - F0 at its last, so its
+cost never exceeds the quota Q' + F.
 """
 
 from __future__ import annotations
@@ -46,6 +53,7 @@ def schedule_chunks(cache_seqlens: Sequence[int], num_parts: int,
     if num_parts <= 0:
         raise ValueError("num_parts must be positive")
     F = int(fixed_overhead)
+    F0 = F // 2                     # overhead units ahead of a request's pages
     P = [_pages(n) for n in cache_seqlens]
     start = 0                       # C_b: where request b begins on the cost line
     total = sum(p + F for p in P if p > 0)
@@ -55,7 +63,7 @@ def schedule_chunks(cache_seqlens: Sequence[int], num_parts: int,
         if p_b == 0:
             continue
         for page in range(p_b):
-            part = (start + F + page) // width
+            part = (start + F0 + page) // width
             if chunks and chunks[-1][0] == part and chunks[-1][1] == b:
                 chunks[-1] = (part, b, chunks[-1][2], page + 1)
             else:

@@ -84,7 +84,7 @@ def _brute_schedule(seqlens, num_parts, F):
     units = []
     for b, p in enumerate(P):
         if p:
-            units += [None] * F + [(b, i) for i in range(p)]
+            units += [None] * (F // 2) + [(b, i) for i in range(p)] + [None] * (F - F // 2)
     width = max(1, -(-len(units) // num_parts))
     owner = {}
     for pos, u in enumerate(units):
