@@ -9,11 +9,14 @@
 // so any finite scale is applied without rounding c * code.
 //
 // Waves: wave w = 2 kh + ch takes keys 32 kh .. +32 of every page (its own
-// online softmax) and output columns 256 ch .. +256.  Its scores S^T come from
-// 16x16x32 MFMAs over the 16 rows (Q fragments in registers, K operands from
-// 16-byte LDS reads, each feeding two MFMAs: the contraction runs over the 576
-// columns in the order in which a lane's 16 codes arrive, and the Q fragments
-// are loaded in that order); P . V uses 16x16x32 MFMAs over the 32 keys, the V^T
+// online softmax) and output columns 256 ch .. +256.  The two waves of a key
+// half (siblings ch = 0, 1) each form one of its two 16-key score tiles, S^T
+// for keys 32 kh + 16 ch .. +16, from 16x16x32 MFMAs over the 16 rows (Q
+// fragments in registers, K operands from 16-byte LDS reads, each feeding two
+// MFMAs: the contraction runs over the 576 columns in the order in which a
+// lane's 16 codes arrive, and the Q fragments are loaded in that order), and
+// swap tiles through LDS, so no score is formed twice and both run the same
+// softmax over the 32 keys; P . V uses 16x16x32 MFMAs over the 32 keys, the V^T
 // operand from one 8-bit transposed LDS read per 16 columns (within a 16-lane
 // group, lane 2r + h addresses key row r, columns 8h .. 8h+7, and lane i
 // receives column i of the eight rows).  The two key halves merge once per
@@ -42,6 +45,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
   __shared__ float sc2_raw[kWaves * 64];
   __shared__ float sc3_raw[kWaves * 64];
   __shared__ float ml_s[2][16][2];           // key half 1: (m, l) of each row, per column half
+  __shared__ f32x4 sx_s[kWaves][64];         // each wave's 16-key score tile, for its sibling
   __shared__ MergeLds<16> merge_s;
   auto buf = [&](auto ic) -> MLA_LDS char* {
     constexpr int i = decltype(ic)::value & 3;
@@ -126,32 +130,33 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
       // The operand reads of a step are issued early and together: with one
       // wave per SIMD nothing else hides the LDS latency.  First the V
       // operands of the whole step (they do not depend on the scores), then
-      // the K operands of score tile 0, and those of tile 1 as tile 0's
-      // registers free up.
+      // the K operands of this wave's score tile.
       const MLA_LDS char* vp = kb + vrow * kRow8 + vh * 8;
       u32x2 vw[16];
 #pragma unroll
       for (int ct = 0; ct < 16; ++ct) vw[ct] = ld_lds_tr8(vp + (((16 * ch + ct) ^ vrot) << 4));
-      // S^T: keys 32kh + 16kt + 4g .. +4 of row li (rot8 of row 32kh + 16kt + li
-      // is krot ^ 2kt: kt is bit 4 of the row)
-      const MLA_LDS char* rp0 = kb + (32 * kh + li) * kRow8;
-      const MLA_LDS char* rp1 = rp0 + 16 * kRow8;
-      u32x4 k0[9], k1[9];
+      // S^T of this wave's 16-key tile kt = ch (keys 32kh + 16ch + 4g .. +4 of row
+      // li; rot8 of row 32kh + 16ch + li is krot ^ 2ch); the sibling wave (same
+      // key half, other column half) forms the other tile, and the two swap
+      // tiles through LDS
+      const MLA_LDS char* rp = kb + (32 * kh + 16 * ch + li) * kRow8;
+      const int rrot = krot ^ (2 * ch);
+      u32x4 k0[9];
 #pragma unroll
-      for (int m = 0; m < 9; ++m) k0[m] = ld_lds16(rp0 + (((4 * m + g) ^ krot) << 4));
+      for (int m = 0; m < 9; ++m) k0[m] = ld_lds16(rp + (((4 * m + g) ^ rrot) << 4));
       const float ksc = scaled ? sbuf(Hc)[0] : 1.f;
-      f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 own = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 9; ++m) {
-        sc[0] = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][0], k0[m][1]}), qf[2 * m], sc[0]);
-        sc[0] = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][2], k0[m][3]}), qf[2 * m + 1], sc[0]);
-        k1[m] = ld_lds16(rp1 + (((4 * m + g) ^ krot ^ 2) << 4));
+        own = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][0], k0[m][1]}), qf[2 * m], own);
+        own = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][2], k0[m][3]}), qf[2 * m + 1], own);
       }
-#pragma unroll
-      for (int m = 0; m < 9; ++m) {
-        sc[1] = Dt<T>::mfma32(codes8_to_bf16(u32x2{k1[m][0], k1[m][1]}), qf[2 * m], sc[1]);
-        sc[1] = Dt<T>::mfma32(codes8_to_bf16(u32x2{k1[m][2], k1[m][3]}), qf[2 * m + 1], sc[1]);
-      }
+      sx_s[wave][lane] = own;
+      lds_barrier();
+      const f32x4 sib = sx_s[wave ^ 1][lane];
+      f32x4 sc[2];
+      sc[0] = ch == 0 ? own : sib;
+      sc[1] = ch == 0 ? sib : own;
       // online softmax of row li over this wave's 32 keys
       float x[8] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1], sc[1][2], sc[1][3]};
       const int key0 = (c.lo + s) * kPage + 32 * kh + 4 * g;
