@@ -26,8 +26,8 @@ every request).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
 --workload N times one workload alone: 1-5 as above, 6, 11 and 12 the fp8-cache
-variants of 3, 2 and 5, 13 and 14 those of 2 and 5 with the fp8 query-key
-product as well, and 7-10 the paged grouped-query (MHA) path (schedule
+variants of 3, 2 and 5, 13, 14 and 15 those of 2, 5 and 3 with the fp8
+query-key product as well, and 7-10 the paged grouped-query (MHA) path (schedule
 mha_get_metadata, split-KV kernel and combine over separate K and V caches).
 """
 
@@ -76,7 +76,7 @@ KERNEL_SOURCES = {
 def mla_kernel_name(w) -> str:
     """The split-KV kernel that runs a workload."""
     if w.kv == "fp8":
-        return "splitkv_wide_fp8_kernel" if w.rows > 16 or w.qk8 else "splitkv_fp8_kernel"
+        return "splitkv_wide_fp8_kernel" if w.rows > 16 else "splitkv_fp8_kernel"
     return "splitkv_wide_kernel" if w.rows > 16 else "splitkv_narrow_kernel"
 
 
@@ -784,8 +784,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=None,
-                    help="one workload only, 1..14 (default: the five configurations 1-5, headline 2); 6, 11 "
-                         "and 12 are 3, 2 and 5 with an fp8 cache, 13 and 14 are 11 and 12 with the fp8 "
+                    help="one workload only, 1..15 (default: the five configurations 1-5, headline 2); 6, 11 "
+                         "and 12 are 3, 2 and 5 with an fp8 cache, 13, 14 and 15 are 11, 12 and 6 with the fp8 "
                          "query-key product, 7-10 use the MHA path (7-9 GQA, 9 with fp8 K/V; 10 multi-query)")
     ap.add_argument("--copies", type=int, default=2, help="independent KV caches rotated per step")
     ap.add_argument("--no-reference", action="store_true",

@@ -105,7 +105,7 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
  * runs on the fp8 matrix instructions from the cached codes directly.  The
  * softmax and the value product are those of MLA_KV_FP8_E4M3.  The result
  * is the attention of the dequantized q over the dequantized cache; any
- * s_q*h_q (the 64-row kernel runs every shape). */
+ * s_q*h_q. */
 typedef enum { MLA_KV_SAME = 0, MLA_KV_FP8_E4M3 = 1, MLA_KV_FP8_E4M3_QK8 = 2 } mla_kv_dtype;
 
 /* Text of the last error raised on the calling thread ("" if none); never NULL.

@@ -260,12 +260,11 @@ mla_status launch_splitkv(const mla_decode_args* args, const mla::DecodeParams& 
   const int tile = tile_rows(p.rows);
   const int m_blocks = (p.rows + tile - 1) / tile;
   hipStream_t hs = stream;
-  // the fp8 query-key product exists in the 64-row kernel only, which also
-  // takes up to 16 rows (one row tile, the rows past them masked)
-  hipError_t e = p.qk8        ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
-                 : tile == 16 ? mla::launch_splitkv_narrow(p, args->dtype, hs)
-                 : p.kv_fp8   ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
-                              : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
+  // up to 16 rows: the 16-row kernels (an fp8 cache, with either score
+  // product, goes to the fp8 one); more: the 64-row kernels
+  hipError_t e = tile == 16 ? mla::launch_splitkv_narrow(p, args->dtype, hs)
+                 : p.kv_fp8 ? mla::launch_splitkv_wide_fp8(p, m_blocks, hs)
+                            : mla::launch_splitkv_wide(p, args->dtype, m_blocks, hs);
   if (e != hipSuccess) return hip_fail(e, "split-KV launch");
   return ok();
 }

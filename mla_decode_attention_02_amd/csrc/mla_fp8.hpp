@@ -66,12 +66,16 @@ __device__ __forceinline__ void load_q_frag8(const DecodeParams& p, int b, int r
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Operand layout of the 16x16x128 fp8 MFMA as used here: within a lane group
-// g (lanes 16g .. 16g+15, one row each), step m covers columns
-// 128m + 32g .. +32, byte j of the lane's eight registers being column
-// 128m + 32g + j; the same for the Q and K operands (the unit pairs byte j of
-// a lane group in both).  Step 4 holds columns 512 .. 575 in groups 0 and 1
-// and zeros in groups 2 and 3.
+// g (lanes 16g .. 16g+15, one row each), step m covers the 16-column chunks
+// 8m + g (bytes 0..15 of the lane's eight registers) and 8m + 4 + g (bytes
+// 16..31); the same for the Q and K operands (the unit pairs byte j of a lane
+// group in both, whatever columns it stands for).  So each of a step's two
+// 16-byte K reads takes four consecutive chunks across the lane groups, the
+// order of the 16-bit score reads.  Step 4 holds chunks 32 .. 35 (columns
+// 512 .. 575) in its first half and zeros in its second.
 constexpr int kQ8Steps = 5;
+// first column of half h (0, 1) of step m for lane group g
+__device__ __forceinline__ int q8_col(int m, int h, int g) { return 128 * m + 64 * h + 16 * g; }
 
 __device__ __forceinline__ int q8_exponent(float amax) {
   if (!(amax > 0.f)) return 0;
@@ -90,10 +94,11 @@ __device__ __forceinline__ void load_q_codes8(const DecodeParams& p, int b, int 
   const bool live = row < p.rows;
   const int tok = live ? row / p.h_q : 0;
   const int head = live ? row - tok * p.h_q : 0;
-  const __bf16* base = (const __bf16*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2 + 32 * g;
+  const __bf16* base = (const __bf16*)p.q + b * p.q_s0 + tok * p.q_s1 + head * p.q_s2;
+  // eight columns: h = 0, 1 the first half of step m, h = 2, 3 the second
   auto raw = [&](int m, int h) {
-    const bool in = live && (m < 4 || g < 2);
-    return in ? *(const u32x4*)(base + 128 * m + 8 * h) : u32x4{0, 0, 0, 0};
+    const bool in = live && (m < kQ8Steps - 1 || h < 2);
+    return in ? *(const u32x4*)(base + q8_col(m, h >> 1, g) + 8 * (h & 1)) : u32x4{0, 0, 0, 0};
   };
   auto val = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xFFFF0000u) : (w << 16)); };
   float amax = 0.f;
@@ -115,7 +120,7 @@ __device__ __forceinline__ void load_q_codes8(const DecodeParams& p, int b, int 
       const u32x4 w = raw(m, h);
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2) {
-        // dword 2h + d2 of the operand: columns 8h + 4 d2 .. +4
+        // dword 2h + d2 of the operand: four columns of raw(m, h)
         const uint32_t w0 = w[2 * d2], w1 = w[2 * d2 + 1];
         int c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(val(w0, 0), -k), ldexpf(val(w0, 1), -k), 0, false);
         c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(val(w1, 0), -k), ldexpf(val(w1, 1), -k), c, true);

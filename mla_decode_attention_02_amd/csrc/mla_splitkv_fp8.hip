@@ -31,6 +31,10 @@
 
 namespace mla {
 
+// kQ8: the query rows are taken into fp8 too (load_q_codes8) and each score
+// tile comes from five 16x16x128 fp8 MFMAs on the cached codes, with the
+// operand layout of the 64-row fp8 kernel (the page images share it).
+template <bool kQ8>
 __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p) {
   typedef __bf16 T;
   __shared__ __attribute__((aligned(1024))) char b0_raw[kPage8];
@@ -89,8 +93,11 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
   for_each_chunk(p, [&](const Chunk& c) {
     BlockWindow bw;
     bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
-    u32x4 qf[18];
-    load_q_frag8(p, c.b, li, g, qf);
+    u32x4 qf[kQ8 ? 1 : 18];
+    i32x8 qc[kQ8 ? kQ8Steps : 1];
+    float qscale = 1.f;                       // 2^k of the row's fp8 codes
+    if constexpr (kQ8) load_q_codes8(p, c.b, li, g, qc, qscale);
+    else load_q_frag8(p, c.b, li, g, qf);
     const int cnt = li < p.rows ? visible_count(c.n, p.s_q, li / p.h_q, p.causal) : 0;
     const int npg = c.hi - c.lo;
 
@@ -141,16 +148,32 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
       // tiles through LDS
       const MLA_LDS char* rp = kb + (32 * kh + 16 * ch + li) * kRow8;
       const int rrot = krot ^ (2 * ch);
-      u32x4 k0[9];
-#pragma unroll
-      for (int m = 0; m < 9; ++m) k0[m] = ld_lds16(rp + (((4 * m + g) ^ rrot) << 4));
-      const float ksc = scaled ? sbuf(Hc)[0] : 1.f;
       f32x4 own = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kQ8) {
+        // K operand of step m: chunks 8m + g and 8m + 4 + g of the key's row
+        // (swizzled); the second half of step 4 lies past the row: zeros
+        auto kop = [&](int m) {
+          const u32x4 lo = ld_lds16(rp + (((8 * m + g) ^ rrot) << 4));
+          const u32x4 hi = m < kQ8Steps - 1 ? ld_lds16(rp + (((8 * m + 4 + g) ^ rrot) << 4)) : u32x4{0, 0, 0, 0};
+          return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        i32x8 ka[kQ8Steps];
 #pragma unroll
-      for (int m = 0; m < 9; ++m) {
-        own = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][0], k0[m][1]}), qf[2 * m], own);
-        own = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][2], k0[m][3]}), qf[2 * m + 1], own);
+        for (int m = 0; m < kQ8Steps; ++m) ka[m] = kop(m);
+#pragma unroll
+        for (int m = 0; m < kQ8Steps; ++m)
+          own = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m], qc[m], own, 0, 0, 0, 127, 0, 127);
+      } else {
+        u32x4 k0[9];
+#pragma unroll
+        for (int m = 0; m < 9; ++m) k0[m] = ld_lds16(rp + (((4 * m + g) ^ rrot) << 4));
+#pragma unroll
+        for (int m = 0; m < 9; ++m) {
+          own = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][0], k0[m][1]}), qf[2 * m], own);
+          own = Dt<T>::mfma32(codes8_to_bf16(u32x2{k0[m][2], k0[m][3]}), qf[2 * m + 1], own);
+        }
       }
+      const float ksc = scaled ? sbuf(Hc)[0] : 1.f;
       sx_s[wave][lane] = own;
       lds_barrier();
       const f32x4 sib = sx_s[wave ^ 1][lane];
@@ -160,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
       // online softmax of row li over this wave's 32 keys
       float x[8] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1], sc[1][2], sc[1][3]};
       const int key0 = (c.lo + s) * kPage + 32 * kh + 4 * g;
-      const float sl = p.scale_log2 * ksc;
+      const float sl = p.scale_log2 * ksc * qscale;          // qscale: 2^k (exact), or 1
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -244,7 +267,8 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_fp8_kernel(DecodeParams p
 }
 
 hipError_t launch_splitkv_fp8(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(splitkv_fp8_kernel, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
+  if (p.qk8) hipLaunchKernelGGL(splitkv_fp8_kernel<true>, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
+  else hipLaunchKernelGGL(splitkv_fp8_kernel<false>, dim3(p.num_parts, 1), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

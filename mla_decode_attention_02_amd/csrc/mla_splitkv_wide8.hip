@@ -169,14 +169,12 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p
         const MLA_LDS char* rp1 = rp0 + 16 * kRow8;
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
         if constexpr (kQ8) {
-          // K operand of step m: chunks 8m + 2g and 8m + 2g + 1 of the key's
-          // row (one swizzled pair); zeros past the row (step 4, groups 2, 3)
+          // K operand of step m: chunks 8m + g and 8m + 4 + g of the key's row
+          // (swizzled); the second half of step 4 lies past the row: zeros
           auto kop = [&](const MLA_LDS char* rp, int rot, int m) {
-            const u32x4 lo = ld_lds16(rp + (((8 * m + 2 * g) ^ rot) << 4));
-            const u32x4 hi = ld_lds16(rp + (((8 * m + 2 * g + 1) ^ rot) << 4));
-            const bool in = m < 4 || g < 2;
-            return i32x8{in ? (int)lo[0] : 0, in ? (int)lo[1] : 0, in ? (int)lo[2] : 0, in ? (int)lo[3] : 0,
-                         in ? (int)hi[0] : 0, in ? (int)hi[1] : 0, in ? (int)hi[2] : 0, in ? (int)hi[3] : 0};
+            const u32x4 lo = ld_lds16(rp + (((8 * m + g) ^ rot) << 4));
+            const u32x4 hi = m < kQ8Steps - 1 ? ld_lds16(rp + (((8 * m + 4 + g) ^ rot) << 4)) : u32x4{0, 0, 0, 0};
+            return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           };
           // both tiles' operands two steps ahead of their MFMAs (a ring of three)
           i32x8 ka[3], kb1[3];

@@ -72,8 +72,9 @@ class Workload:
 
 # The workloads the measurements are quoted on.  Seeds are the index, except
 # for the fp8-cache variants 6, 11 and 12: workloads 3, 2 and 5 (same seed,
-# lengths and page table) with an fp8 cache, and 13 and 14: workloads 11 and
-# 12 with the fp8 query-key product as well.  (7..10 are the MHA workloads.)
+# lengths and page table) with an fp8 cache, and 13, 14 and 15: workloads
+# 11, 12 and 6 with the fp8 query-key product as well.  (7..10 are the MHA
+# workloads.)
 WORKLOADS = {
     1: Workload("tiny", 2, 1, 16, "bf16", 1.0, False, seqlens=(64, 100), seed=1,
                 description="B2 s_q1 h_q16 bf16, s_k {64,100}, non-causal"),
@@ -102,6 +103,9 @@ WORKLOADS = {
     14: Workload("longctx_bs4_hq128_fp8kv_qk8", 4, 1, 128, "bf16", 1.0, False,
                  seqlens=(65536, 98304, 131072, 131072), seed=5, kv="fp8", qk8=True,
                  description="workload 12 with q taken into fp8 (per-row power-of-two scale) for an fp8 Q.K^T"),
+    15: Workload("varlen_bs128_hq16_fp8kv_qk8", 128, 1, 16, "bf16", 1.0, False, seqlen_range=(1, 8192), seed=3,
+                 kv="fp8", qk8=True,
+                 description="workload 6 with q taken into fp8 (per-row power-of-two scale) for an fp8 Q.K^T"),
 }
 
 

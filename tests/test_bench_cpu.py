@@ -69,7 +69,8 @@ def test_kernel_attribution():
     # (16 rows or fewer: narrow; more: wide; fp8 cache: the fp8 kernel of the
     # same width; MHA: key split for fp8 caches with small row tiles, else
     # mha_splitkv_kernel)
-    assert [bench.mla_kernel_name(WORKLOADS[i]) for i in (13, 14)] == ["splitkv_wide_fp8_kernel"] * 2
+    assert [bench.mla_kernel_name(WORKLOADS[i]) for i in (13, 14, 15)] == ["splitkv_wide_fp8_kernel"] * 2 + [
+        "splitkv_fp8_kernel"]
     assert [bench.mla_kernel_name(WORKLOADS[i]) for i in (1, 2, 3, 4, 5, 6, 11, 12)] == [
         "splitkv_narrow_kernel", "splitkv_wide_kernel", "splitkv_narrow_kernel", "splitkv_wide_kernel",
         "splitkv_wide_kernel", "splitkv_fp8_kernel", "splitkv_wide_fp8_kernel", "splitkv_wide_fp8_kernel"]

@@ -357,11 +357,13 @@ def test_qk8_unused_slots_and_pages_are_never_read_bitwise(h_q):
     assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
 
 
-def test_qk8_full_size_every_request():
-    # the headline shape with an fp8 cache and the fp8 query-key product
-    w = WORKLOADS[11]
+@pytest.mark.parametrize("idx", [11, 6])
+def test_qk8_full_size_every_request(idx):
+    # the headline shape (64-row kernel) and the 128-request varlen shape
+    # (16-row kernel) with an fp8 cache and the fp8 query-key product
+    w = WORKLOADS[idx]
     _say(f"fp8 Q.K full size: {w.name}")
-    host = workload_inputs(11)
+    host = workload_inputs(idx)
     g = host.to(torch.device("cuda:0"))
     out, lse = api.mla_decode(g.q, g.k_cache, g.block_table, g.cache_seqlens, g.softmax_scale, g.causal,
                               k_scale=g.k_scale, qk_fp8=True)
