@@ -156,6 +156,36 @@ def test_small_parity(s_q, h_q, seqlens, causal, dtype, parts, entry):
     compare(out, lse, ref_o, ref_l, tag)
 
 
+# Many row tiles per request: s_q * h_q of 512 to 1024 rows (8 to 16 tiles of
+# 64, so the default partition count falls to 32 or 16 per tile), causal and
+# not, with ragged lengths; the fp8 cache and the fp8 query-key product too.
+MANY_ROWS = [
+    # (s_q, h_q, seqlens, causal, dtype, kv, qk8, num_parts)
+    (4, 128, (100, 700), True, "bf16", "same", False, None),
+    (8, 128, (65, 300), True, "fp16", "same", False, 3),
+    (6, 100, (129,), False, "bf16", "same", False, 2),
+    (4, 128, (200, 9, 64), True, "bf16", "fp8", False, None),
+    (4, 128, (300, 1), True, "bf16", "fp8", True, 5),
+]
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("s_q,h_q,seqlens,causal,dtype,kv,qk8,parts", MANY_ROWS,
+                         ids=[f"sq{c[0]}_hq{c[1]}_{c[5]}{'_qk8' if c[6] else ''}_p{c[7]}" for c in MANY_ROWS])
+def test_many_row_tiles(s_q, h_q, seqlens, causal, dtype, kv, qk8, parts, entry):
+    tag = f"many rows {entry} s_q={s_q} h_q={h_q} seqlens={seqlens} causal={causal} {dtype} {kv} qk8={qk8} parts={parts}"
+    _say(tag)
+    x = make_inputs(len(seqlens), s_q, h_q, dtype, seqlens=seqlens, causal=causal,
+                    seed=sum(seqlens) + s_q * h_q, poison=True, extra_pages=2, kv_dtype=kv)
+    out, lse, _ = run(x, parts, entry, qk_fp8=qk8)
+    if qk8:
+        q = quantize_q_rows(x.q)
+    else:
+        q = x.q
+    ref_o, ref_l = oracle_decode(q, kv64(x), x.block_table, x.cache_seqlens, x.softmax_scale, causal)
+    compare(out, lse, ref_o, ref_l, tag)
+
+
 @pytest.mark.parametrize("entry", ENTRIES)
 def test_empty_request_and_masked_rows(entry):
     _say(f"empty request / fully masked causal rows ({entry})")
