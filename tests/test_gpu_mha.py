@@ -95,6 +95,9 @@ EDGE = [
     (1, 12, 4, 128, (5000,), False, "bf16", 17),           # one long request cut into many pieces
     (1, 32, 1, 128, (70, 300), False, "fp16", 4),          # 32 rows: row split, two idle waves
     (2, 64, 2, 256, (40, 129), True, "fp16", 3),           # 64 rows, d = 256: row split, fp16
+    (4, 64, 1, 128, (100, 700), True, "bf16", None),       # 256 rows: four row blocks
+    (2, 128, 1, 64, (65, 300, 1), True, "bf16", 2),        # 256 rows at d = 64
+    (8, 32, 1, 256, (65, 300), True, "fp16", 3),           # 256 rows at d = 256
 ]
 
 
@@ -240,6 +243,7 @@ FP8_EDGE = [
     (3, 32, 1, 64, (2, 129, 300), True, "amax", 3),        # d=64, 96 rows: key split, four tiles, two row blocks
     (1, 32, 1, 256, (33, 200), False, "amax", 2),          # d=256, 32 rows: fp8 row split
     (2, 16, 1, 256, (1, 65, 130), True, "none", 3),        # d=256, 32 rows, causal: fp8 row split
+    (4, 64, 1, 128, (300, 9), True, "amax", None),         # 256 rows: four row blocks, fp8
 ]
 
 
