@@ -72,6 +72,21 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
   if (wave < 4) {
     // -------------------------------------------------------- score waves --
     const int srow = wave * 16 + li;                          // tile row of this lane
+    // This lane's source offsets for the wave's nine loads of a half page
+    // (value rows 8w .. 8w+7, then rope rows 8w .. 8w+7), for either half of
+    // a page: computed once, so a load costs no address arithmetic in the
+    // MFMA stream.
+    int dof[2][9];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * wave + i;
+        dof[h][i] = ((lane ^ swz_v(r)) << 4) + (h * kHalfRows + r) * row_bytes;
+      }
+      const int rr = 8 * wave + (lane >> 3);
+      dof[h][8] = (h * kHalfRows + rr) * row_bytes + 1024 + (((lane & 7) ^ swz_r(rr)) << 4);
+    }
     for_each_chunk(p, [&](const Chunk& c) {
       BlockWindow bw;
       bw.init(p.block_table + (int64_t)c.b * p.bt_s, c.lo, c.hi, lane);
@@ -85,7 +100,10 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
       // Loads of half page hh: this wave moves value rows 8w .. 8w+7 (piece
       // i < 8) and rope rows 8w .. 8w+7 (piece 8).  Past the end of the chunk
       // an empty descriptor keeps the count of loads in flight uniform
-      // (every lane out of range, no memory access).
+      // (every lane out of range, no memory access).  With loop-invariant
+      // offsets the compiler would gather the loads at one point of the step,
+      // which stalls the MFMA stream; the scheduling barriers keep each one
+      // where it is issued.
       auto page_desc = [&](int hh) {
         const bool real = hh < nh;
         const int pg = c.lo + (hh >> 1);
@@ -94,14 +112,10 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_kernel(DecodeParams p) {
       auto piece = [&](auto ic, int hh, BufRsrc pg, int i) {
         MLA_LDS char* hb = hbuf(ic);
         const int half = hh & 1;
-        int ln = lane;                 // opaque: offsets are rebuilt, not kept live
-        asm volatile("" : "+v"(ln));
-        if (i < 8) {
-          const int r = 8 * wave + i;
-          dma16<kWideAux>(pg, hb + r * 1024, ((ln ^ swz_v(r)) << 4) + (half * kHalfRows + r) * row_bytes, 0);
-        } else {
-          dma_rope_rows8<kWideAux>(pg, hb, half, wave, row_bytes, ln);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 8) dma16<kWideAux>(pg, hb + (8 * wave + i) * 1024, half ? dof[1][i] : dof[0][i], 0);
+        else dma16<kWideAux>(pg, hb + kHalfRopeOff + wave * 1024, half ? dof[1][8] : dof[0][8], 0);
+        __builtin_amdgcn_sched_barrier(0);
       };
       {
         const BufRsrc pg0 = page_desc(0), pg1 = page_desc(1);
