@@ -105,6 +105,9 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p
       const int r = q / 36;
       doff[i] = r * row_bytes + (((q - r * 36) ^ rot8(r)) << 4);
     }
+    int doff2[kDmaW8];                          // the same for the second half of a page
+#pragma unroll
+    for (int i = 0; i < kDmaW8; ++i) doff2[i] = doff[i] + kHalfRows * row_bytes;
     const bool pad_wave = wave == 3;
     const BufRsrc none = page_rsrc((const char*)p.k, 0);
     // the page scales (no memory access without them)
@@ -144,13 +147,20 @@ __global__ __launch_bounds__(512, 1) void splitkv_wide_fp8_kernel(DecodeParams p
       // load i of half page hh into buffer ic: pieces 0..4, then the scale
       auto load = [&](auto ic, int hh, const HalfSrc& h, auto i_c) {
         constexpr int i = decltype(i_c)::value;
+        // With the fp8 score product the loads sit one per MFMA step; the
+        // scheduling barriers keep the compiler from gathering them (the
+        // offsets are loop-invariant), which measured 2-4 % faster there and
+        // no faster with the bf16 score product.
+        if constexpr (kQ8) __builtin_amdgcn_sched_barrier(0);
         if constexpr (i < kDmaW8) {
           const BufRsrc src = (i >= 3 && pad_wave) ? none : h.rows;
-          dma16<kWideAux>(src, hbuf(ic) + (wave * kDmaW8 + i) * 1024, doff[i] + (hh & 1) * kHalfRows * row_bytes, 0);
+          const int off = kQ8 ? ((hh & 1) ? doff2[i] : doff[i]) : doff[i] + (hh & 1) * kHalfRows * row_bytes;
+          dma16<kWideAux>(src, hbuf(ic) + (wave * kDmaW8 + i) * 1024, off, 0);
         } else {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(scales, (MLA_LDS void*)(sbuf(ic) + wave * 64), 4, 0,
                                                    h.scale_off, 0, 0);
         }
+        if constexpr (kQ8) __builtin_amdgcn_sched_barrier(0);
       };
       {
         const HalfSrc h0 = half_src(0), h1 = half_src(1);
